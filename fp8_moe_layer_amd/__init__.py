@@ -1,0 +1,311 @@
+"""fp8_moe_layer_amd -- W8A8 FP8 Mixture-of-Experts layer forward for AMD MI355X.
+
+Thin ctypes binding over the gfx950 HIP library ``libfp8moe.so`` (C ABI in
+``include/fp8moe.h``).  Every step of the layer runs in the library's
+kernels; this module only turns torch tensors into pointers and the current
+torch stream into a hipStream_t.  There is no CPU path: importing the package
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import pathlib
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libfp8moe.so"
+
+MOE_F_NO_REQUANT = 1
+MAX_EXPERTS = 512
+MAX_K = 32
+
+if not LIB_PATH.exists():
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python fp8_moe_layer_amd/build.py` first (there is no CPU fallback)")
+
+_lib = C.CDLL(str(LIB_PATH))
+
+_vp = C.c_void_p
+_i32 = C.c_int32
+
+
+class Dims(C.Structure):
+    _fields_ = [("T", _i32), ("d", _i32), ("f", _i32), ("E", _i32), ("k_max", _i32),
+                ("n_shared", _i32), ("block_m", _i32), ("flags", C.c_uint32)]
+
+
+class _Weights(C.Structure):
+    _fields_ = [(n, _vp) for n in ("w_gate", "w_up", "s_gate", "s_up", "w_down", "s_down",
+                                   "ws_gate", "ws_up", "ws_down", "ss_gate", "ss_up", "ss_down")]
+
+
+def _sig(name, restype, *argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = list(argtypes)
+    return fn
+
+
+_DP = C.POINTER(Dims)
+_WP = C.POINTER(_Weights)
+_quantize_rows = _sig("moe_quantize_rows", _i32, _vp, _i32, _i32, _vp, _vp, _vp)
+_router_logits = _sig("moe_router_logits", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
+_route_topk = _sig("moe_route_topk", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
+_capacity = _sig("moe_capacity", C.c_int64, _i32, _i32, _i32, _i32)
+_permute = _sig("moe_permute", _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp)
+_gate_up = _sig("moe_expert_gate_up", _i32, _DP, _i32, _vp, _vp, _vp, _vp, _WP, _vp, _vp)
+_down = _sig("moe_expert_down", _i32, _DP, _i32, _vp, _vp, _vp, _vp, _vp, _WP, _vp, _vp)
+_combine = _sig("moe_combine", _i32, _DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp)
+_workspace_bytes = _sig("moe_workspace_bytes", C.c_size_t, _DP)
+_fused_forward = _sig("moe_fused_forward", _i32, _DP, _vp, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _vp,
+                      _vp, C.c_size_t, _vp)
+_status_str = _sig("moe_status_str", C.c_char_p, _i32)
+_last_error = _sig("moe_last_error", C.c_char_p)
+_abi_version = _sig("moe_abi_version", _i32)
+_debug_stage_events = _sig("moe_debug_stage_events", _i32, C.POINTER(_vp), _i32)
+
+N_STAGE_EVENTS = 9
+STAGES = ("quantize", "router", "topk", "permute", "gate_up", "requant", "down", "combine")
+
+ABI_VERSION = int(_abi_version())
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        detail = _last_error().decode()
+        super().__init__(f"{_status_str(status).decode()} ({status}): {detail}")
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoEError(status)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("fp8_moe_layer_amd works on device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def set_stage_events(handles):
+    """Make moe_fused_forward (on this thread) record the given hipEvent_t
+    handles around its stages (instrumentation); None stops it."""
+    if handles is None:
+        _check(_debug_stage_events(None, 0))
+        return None
+    arr = (_vp * len(handles))(*handles)
+    _check(_debug_stage_events(arr, len(handles)))
+    return arr  # the caller keeps this alive while the events are in use
+
+
+# --------------------------------------------------------------------------- steps
+
+def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None, scale=None, stream=None):
+    """Per-row e4m3 quantisation: (codes uint8 like x, fp32 scale per row)."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if scale is None else scale
+    _check(_quantize_rows(_ptr(x, torch.float32), rows, cols, _ptr(q, torch.uint8),
+                          _ptr(scale, torch.float32), _stream(stream)))
+    return q, scale
+
+
+def router_logits(x, w_router, bias=None, stream=None):
+    T, d = x.shape
+    E = w_router.shape[0]
+    out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(_router_logits(_ptr(x, torch.float32), _ptr(w_router, torch.float32),
+                          _ptr(bias, torch.float32), T, d, E, _ptr(out), _stream(stream)))
+    return out
+
+
+def route_topk(logits, k_max: int, k_per_token=None, stream=None):
+    T, E = logits.shape
+    ids = torch.empty((T, k_max), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k_max), dtype=torch.float32, device=logits.device)
+    _check(_route_topk(_ptr(logits, torch.float32), T, E, k_max, _ptr(k_per_token, torch.int32),
+                       _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
+
+
+def capacity(T: int, E: int, k_max: int, block_m: int) -> int:
+    return int(_capacity(T, E, k_max, block_m))
+
+
+def permute(topk_ids, E: int, block_m: int, cap: Optional[int] = None, stream=None) -> dict:
+    T, K = topk_ids.shape
+    cap = capacity(T, E, K, block_m) if cap is None else cap
+    dev = topk_ids.device
+    z = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    out = dict(sorted_pairs=z(cap), expert_offsets=z(E + 1), block_expert=z((cap + block_m - 1) // block_m),
+               inv_pairs=z(T * K), n_blocks=z(1))
+    _check(_permute(_ptr(topk_ids, torch.int32), T, E, K, block_m, cap, _ptr(out["sorted_pairs"]),
+                    _ptr(out["expert_offsets"]), _ptr(out["block_expert"]), _ptr(out["inv_pairs"]),
+                    _ptr(out["n_blocks"]), _stream(stream)))
+    out["capacity"] = cap
+    return out
+
+
+# --------------------------------------------------------------------------- weights
+
+@dataclass
+class DeviceWeights:
+    """e4m3 expert weights (uint8 codes) with fp32 per-output-channel scales."""
+    w_gate: torch.Tensor  # [E, f, d]
+    w_up: torch.Tensor
+    s_gate: torch.Tensor  # [E, f]
+    s_up: torch.Tensor
+    w_down: torch.Tensor  # [E, d, f]
+    s_down: torch.Tensor  # [E, d]
+    ws_gate: Optional[torch.Tensor] = None
+    ws_up: Optional[torch.Tensor] = None
+    ss_gate: Optional[torch.Tensor] = None
+    ss_up: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None
+    ss_down: Optional[torch.Tensor] = None
+
+    @property
+    def E(self) -> int:
+        return int(self.w_gate.shape[0])
+
+    @property
+    def f(self) -> int:
+        return int(self.w_gate.shape[1])
+
+    @property
+    def d(self) -> int:
+        return int(self.w_gate.shape[2])
+
+    @property
+    def n_shared(self) -> int:
+        return 0 if self.ws_gate is None else int(self.ws_gate.shape[0])
+
+    def struct(self) -> _Weights:
+        p = lambda t: _ptr(t)
+        return _Weights(p(self.w_gate), p(self.w_up), p(self.s_gate), p(self.s_up), p(self.w_down),
+                        p(self.s_down), p(self.ws_gate), p(self.ws_up), p(self.ws_down),
+                        p(self.ss_gate), p(self.ss_up), p(self.ss_down))
+
+    @staticmethod
+    def empty(E: int, d: int, f: int, n_shared: int = 0, device="cuda") -> "DeviceWeights":
+        u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=device)
+        f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=device)
+        w = DeviceWeights(u8(E, f, d), u8(E, f, d), f32(E, f), f32(E, f), u8(E, d, f), f32(E, d))
+        if n_shared:
+            w.ws_gate, w.ws_up, w.ws_down = u8(n_shared, f, d), u8(n_shared, f, d), u8(n_shared, d, f)
+            w.ss_gate, w.ss_up, w.ss_down = f32(n_shared, f), f32(n_shared, f), f32(n_shared, d)
+        return w
+
+    def set_expert(self, which: str, e: int, w32: torch.Tensor, shared: bool = False):
+        """Quantise one fp32 expert matrix per output channel into slot e."""
+        pre = "ws_" if shared else "w_"
+        spre = "ss_" if shared else "s_"
+        quantize_rows(w32.contiguous(), getattr(self, pre + which)[e], getattr(self, spre + which)[e])
+
+
+# --------------------------------------------------------------------------- expert stages
+
+def dims(T, d, f, E, k_max, n_shared=0, block_m=16, no_requant=False) -> Dims:
+    return Dims(T, d, f, E, k_max, n_shared, block_m, MOE_F_NO_REQUANT if no_requant else 0)
+
+
+def expert_gate_up(dm: Dims, perm: dict, xq, sx, w: DeviceWeights, stream=None):
+    rows = perm["capacity"] + dm.n_shared * dm.T
+    h = torch.zeros((rows, dm.f), dtype=torch.float32, device=xq.device)
+    ws = w.struct()
+    _check(_gate_up(C.byref(dm), perm["capacity"], _ptr(xq, torch.uint8), _ptr(sx, torch.float32),
+                    _ptr(perm["sorted_pairs"]), _ptr(perm["expert_offsets"]), C.byref(ws), _ptr(h),
+                    _stream(stream)))
+    return h
+
+
+def expert_down(dm: Dims, perm: dict, w: DeviceWeights, hq=None, sh=None, h=None, stream=None):
+    rows = perm["capacity"] + dm.n_shared * dm.T
+    dev = (hq if hq is not None else h).device
+    y = torch.zeros((rows, dm.d), dtype=torch.float32, device=dev)
+    ws = w.struct()
+    _check(_down(C.byref(dm), perm["capacity"], _ptr(hq, torch.uint8), _ptr(sh, torch.float32),
+                 _ptr(h, torch.float32), _ptr(perm["sorted_pairs"]), _ptr(perm["expert_offsets"]),
+                 C.byref(ws), _ptr(y), _stream(stream)))
+    return y
+
+
+def combine(dm: Dims, perm: dict, y, topk_ids, topk_w, stream=None):
+    out = torch.empty((dm.T, dm.d), dtype=torch.float32, device=y.device)
+    _check(_combine(C.byref(dm), perm["capacity"], _ptr(y, torch.float32), _ptr(topk_ids, torch.int32),
+                    _ptr(topk_w, torch.float32), _ptr(perm["inv_pairs"]), _ptr(out), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------- whole layer
+
+def workspace_bytes(dm: Dims) -> int:
+    return int(_workspace_bytes(C.byref(dm)))
+
+
+class MoELayer:
+    """One W8A8 FP8 MoE layer resident on the device.
+
+    forward(x) runs the whole layer (quantise, router, top-k, permutation,
+    gate/up + SiLU*up, requantisation, down projection, combine) in the
+    library's kernels on the current stream.  The workspace is allocated once
+    per token count and reused.
+    """
+
+    def __init__(self, weights: DeviceWeights, w_router: Optional[torch.Tensor], k_max: int,
+                 router_bias: Optional[torch.Tensor] = None, block_m: int = 16,
+                 no_requant: bool = False):
+        self.w = weights
+        self.w_router = w_router
+        self.router_bias = router_bias
+        self.k_max = k_max
+        self.block_m = block_m
+        self.no_requant = no_requant
+        self._ws = {}
+        self._wstruct = weights.struct()
+
+    def dims(self, T: int) -> Dims:
+        return dims(T, self.w.d, self.w.f, self.w.E, self.k_max, self.w.n_shared, self.block_m,
+                    self.no_requant)
+
+    def workspace(self, T: int, device) -> torch.Tensor:
+        ws = self._ws.get(T)
+        if ws is None:
+            n = workspace_bytes(self.dims(T))
+            if n == 0:
+                raise MoEError(int(2))
+            ws = torch.empty(n, dtype=torch.uint8, device=device)
+            self._ws = {T: ws}
+        return ws
+
+    def forward(self, x: torch.Tensor, k_per_token=None, logits_override=None, out=None,
+                topk_ids=None, topk_w=None, stream=None) -> torch.Tensor:
+        T = x.shape[0]
+        dm = self.dims(T)
+        out = torch.empty((T, self.w.d), dtype=torch.float32, device=x.device) if out is None else out
+        ws = self.workspace(T, x.device)
+        _check(_fused_forward(C.byref(dm), _ptr(x, torch.float32), _ptr(self.w_router, torch.float32),
+                              _ptr(self.router_bias, torch.float32), _ptr(k_per_token, torch.int32),
+                              C.byref(self._wstruct), _ptr(logits_override, torch.float32), _ptr(out),
+                              _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), _ptr(ws),
+                              ws.numel(), _stream(stream)))
+        return out
+
+    __call__ = forward

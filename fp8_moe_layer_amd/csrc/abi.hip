@@ -1,0 +1,414 @@
+// abi.hip -- the C ABI (include/fp8moe.h): host-side validation, workspace
+// layout, tile-shape choice and kernel enqueueing.  No allocation, no
+// synchronisation, no state kept between calls except the thread-local error
+// text.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fp8moe.h"
+#include "internal.hpp"
+
+using namespace fp8moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t const *g_stage_events = nullptr;
+
+moe_status fail(moe_status code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool block_m_ok(int32_t bm) { return bm == 1 || bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+moe_status check_dims(const moe_dims *d, const char *fn) {
+  if (!d) return fail(MOE_ERR_NULL, "%s: dims is NULL", fn);
+  if (d->T < 1) return fail(MOE_ERR_SHAPE, "%s: T=%d must be >= 1", fn, d->T);
+  if (d->d < 64 || d->d % 64 || d->d > MOE_MAX_HIDDEN)
+    return fail(MOE_ERR_SHAPE, "%s: d=%d must be a multiple of 64 in [64, %d]", fn, d->d, MOE_MAX_HIDDEN);
+  if (d->f < 64 || d->f % 64) return fail(MOE_ERR_SHAPE, "%s: f=%d must be a positive multiple of 64", fn, d->f);
+  if (d->E < 1 || d->E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "%s: E=%d must be in [1, %d]", fn, d->E, MOE_MAX_EXPERTS);
+  if (d->k_max < 1 || d->k_max > d->E || d->k_max > MOE_MAX_K)
+    return fail(MOE_ERR_SHAPE, "%s: k_max=%d must be in [1, min(E, %d)]", fn, d->k_max, MOE_MAX_K);
+  if (d->n_shared < 0) return fail(MOE_ERR_SHAPE, "%s: n_shared=%d must be >= 0", fn, d->n_shared);
+  if (!block_m_ok(d->block_m))
+    return fail(MOE_ERR_SHAPE, "%s: block_m=%d must be 1, 16, 32, 64 or 128", fn, d->block_m);
+  if (d->flags & ~(uint32_t)MOE_F_NO_REQUANT)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown flags 0x%x", fn, d->flags);
+  // all row indices must fit in int32
+  const int64_t rows = (int64_t)d->T * d->k_max + (int64_t)d->E * (d->block_m - 1) +
+                       (int64_t)d->n_shared * d->T;
+  if (rows * (int64_t)(d->d > d->f ? d->d : d->f) > ((int64_t)1 << 40) || rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_SHAPE, "%s: layer too large (%lld expert rows)", fn, (long long)rows);
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_dims *d, const moe_weights *w, const char *fn) {
+  if (!w) return fail(MOE_ERR_NULL, "%s: weights is NULL", fn);
+  if (!w->w_gate || !w->w_up || !w->w_down || !w->s_gate || !w->s_up || !w->s_down)
+    return fail(MOE_ERR_NULL, "%s: a routed expert weight or scale pointer is NULL", fn);
+  if (d->n_shared > 0 &&
+      (!w->ws_gate || !w->ws_up || !w->ws_down || !w->ss_gate || !w->ss_up || !w->ss_down))
+    return fail(MOE_ERR_NULL, "%s: n_shared=%d but a shared expert pointer is NULL", fn, d->n_shared);
+  const void *p16[] = {w->w_gate, w->w_up, w->w_down, w->ws_gate, w->ws_up, w->ws_down};
+  for (const void *p : p16)
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGN, "%s: weight codes must be 16-byte aligned", fn);
+  const void *p4[] = {w->s_gate, w->s_up, w->s_down, w->ss_gate, w->ss_up, w->ss_down};
+  for (const void *p : p4)
+    if (p && !aligned(p, 4)) return fail(MOE_ERR_ALIGN, "%s: scales must be 4-byte aligned", fn);
+  return MOE_OK;
+}
+
+ExpertWeights to_internal(const moe_weights *w) {
+  return ExpertWeights{w->w_gate,  w->w_up,  w->w_down,  w->s_gate,  w->s_up,  w->s_down,
+                       w->ws_gate, w->ws_up, w->ws_down, w->ss_gate, w->ss_up, w->ss_down};
+}
+
+int64_t capacity_of(int32_t T, int32_t E, int32_t k, int32_t bm) {
+  return (int64_t)T * k + (int64_t)E * (bm - 1);
+}
+
+// Row-pass size for the grouped GEMMs: 16*msub rows per pass, sized so that a
+// decode-sized batch keeps all of an expert's rows in one pass (its weights
+// then stream from HBM once).  mean + 4 sigma of a binomial expert load, in
+// units of 16 rows, rounded up to a power of two, at most 8.
+int32_t choose_msub(const moe_dims *d) {
+  const double mean = (double)d->T * d->k_max / d->E;
+  const double est = mean + 4.0 * sqrt(mean) + 2.0;
+  int32_t m = 1;
+  while (m < 8 && 16.0 * m < est) m <<= 1;
+  return m;
+}
+
+// Workspace layout of moe_fused_forward (all pieces 256-byte aligned).
+struct Layout {
+  size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
+      hq, sh, y, total;
+  int32_t capacity, rows_total, max_items, row_chunk, msub;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout layout_of(const moe_dims *d) {
+  Layout L{};
+  L.capacity = (int32_t)capacity_of(d->T, d->E, d->k_max, d->block_m);
+  L.rows_total = L.capacity + d->n_shared * d->T;
+  L.msub = choose_msub(d);
+  L.row_chunk = 16 * L.msub;
+  L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
+  const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = up256(o + bytes);
+    return at;
+  };
+  L.xq = take(T * d->d);
+  L.sx = take(T * 4);
+  L.logits = take(T * d->E * 4);
+  L.ids = take(P * 4);
+  L.w = take(P * 4);
+  L.sorted = take((size_t)L.capacity * 4);
+  L.offsets = take((size_t)(d->E + 1) * 4);
+  L.block_expert = take((size_t)((L.capacity + d->block_m - 1) / d->block_m) * 4);
+  L.inv = take(P * 4);
+  L.n_blocks = take(4);
+  L.items = take((size_t)L.max_items * sizeof(WorkItem));
+  L.n_items = take(4);
+  L.h = take(R * d->f * 4);
+  L.hq = take(R * d->f);
+  L.sh = take(R * 4);
+  L.y = take(R * d->d * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "unsupported shape";
+    case MOE_ERR_ALIGN: return "misaligned pointer";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return FP8MOE_ABI_VERSION; }
+
+moe_status moe_debug_stage_events(void *const *events, int32_t n_events) {
+  if (!events || n_events == 0) {
+    g_stage_events = nullptr;
+    return ok();
+  }
+  if (n_events < MOE_N_STAGE_EVENTS)
+    return fail(MOE_ERR_SHAPE, "moe_debug_stage_events: %d events given, %d needed", n_events,
+                MOE_N_STAGE_EVENTS);
+  g_stage_events = reinterpret_cast<hipEvent_t const *>(events);
+  return ok();
+}
+
+int64_t moe_capacity(int32_t T, int32_t E, int32_t k_max, int32_t block_m) {
+  return capacity_of(T, E, k_max, block_m);
+}
+
+moe_status moe_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t *q, float *scale,
+                             void *stream) {
+  const char *fn = "moe_quantize_rows";
+  if (!x || !q || !scale) return fail(MOE_ERR_NULL, "%s: x, q and scale are required", fn);
+  if (rows < 0 || cols < 4 || cols % 4)
+    return fail(MOE_ERR_SHAPE, "%s: rows=%d, cols=%d (cols must be a positive multiple of 4)", fn,
+                rows, cols);
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(scale, 4))
+    return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte and q 4-byte aligned", fn);
+  moe_status s = hip_status(launch_quantize_rows(x, rows, cols, q, scale, as_stream(stream)), fn);
+  return s ? s : ok();
+}
+
+moe_status moe_router_logits(const float *x, const float *w_router, const float *bias, int32_t T,
+                             int32_t d, int32_t E, float *logits, void *stream) {
+  const char *fn = "moe_router_logits";
+  if (!x || !w_router || !logits) return fail(MOE_ERR_NULL, "%s: x, w_router and logits are required", fn);
+  if (T < 0 || d < 64 || d % 64 || d > MOE_MAX_HIDDEN || E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "%s: T=%d d=%d E=%d (d multiple of 64 up to %d, E in [1,%d])", fn,
+                T, d, E, MOE_MAX_HIDDEN, MOE_MAX_EXPERTS);
+  if (!aligned(x, 16) || !aligned(w_router, 16))
+    return fail(MOE_ERR_ALIGN, "%s: x and w_router must be 16-byte aligned", fn);
+  moe_status s =
+      hip_status(launch_router(x, w_router, bias, T, d, E, logits, as_stream(stream)), fn);
+  return s ? s : ok();
+}
+
+moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
+                          const int32_t *k_per_token, int32_t *topk_ids, float *topk_w,
+                          void *stream) {
+  const char *fn = "moe_route_topk";
+  if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_NULL, "%s: logits, topk_ids and topk_w are required", fn);
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k_max < 1 || k_max > E || k_max > MOE_MAX_K)
+    return fail(MOE_ERR_SHAPE, "%s: T=%d E=%d k_max=%d", fn, T, E, k_max);
+  moe_status s = hip_status(
+      launch_topk(logits, T, E, k_max, k_per_token, topk_ids, topk_w, as_stream(stream)), fn);
+  return s ? s : ok();
+}
+
+moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
+                       int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
+                       int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
+                       int32_t *n_blocks, void *stream) {
+  const char *fn = "moe_permute";
+  if (!topk_ids || !sorted_pairs || !expert_offsets || !block_expert || !inv_pairs || !n_blocks)
+    return fail(MOE_ERR_NULL, "%s: every array is required", fn);
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k_max < 1 || k_max > MOE_MAX_K ||
+      !block_m_ok(block_m) || (int64_t)T * k_max >= ((int64_t)1 << 30))
+    return fail(MOE_ERR_SHAPE, "%s: T=%d E=%d k_max=%d block_m=%d", fn, T, E, k_max, block_m);
+  if ((int64_t)capacity < capacity_of(T, E, k_max, block_m))
+    return fail(MOE_ERR_SHAPE, "%s: capacity=%d < T*k_max + E*(block_m-1) = %lld", fn, capacity,
+                (long long)capacity_of(T, E, k_max, block_m));
+  moe_status s = hip_status(launch_permute(topk_ids, T, E, k_max, block_m, capacity, sorted_pairs,
+                                           expert_offsets, block_expert, inv_pairs, n_blocks,
+                                           nullptr, nullptr, 0, 0, as_stream(stream)),
+                            fn);
+  return s ? s : ok();
+}
+
+static RowSpace row_space(const moe_dims *d, int32_t capacity, const int32_t *sorted_pairs,
+                          const int32_t *expert_offsets) {
+  RowSpace rs{};
+  rs.T = d->T;
+  rs.d = d->d;
+  rs.f = d->f;
+  rs.E = d->E;
+  rs.S = d->n_shared;
+  rs.k_max = d->k_max;
+  rs.capacity = capacity;
+  rs.sorted_pairs = sorted_pairs;
+  rs.expert_offsets = expert_offsets;
+  return rs;
+}
+
+static moe_status check_stage(const moe_dims *dims, int32_t capacity, const moe_weights *w,
+                              const int32_t *sorted_pairs, const int32_t *expert_offsets,
+                              const char *fn) {
+  moe_status s = check_dims(dims, fn);
+  if (s) return s;
+  if ((s = check_weights(dims, w, fn))) return s;
+  if (!sorted_pairs || !expert_offsets)
+    return fail(MOE_ERR_NULL, "%s: sorted_pairs and expert_offsets are required", fn);
+  const int64_t need = capacity_of(dims->T, dims->E, dims->k_max, dims->block_m);
+  if ((int64_t)capacity < need || (int64_t)capacity + (int64_t)dims->n_shared * dims->T >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_SHAPE, "%s: capacity=%d must be >= %lld", fn, capacity, (long long)need);
+  return MOE_OK;
+}
+
+moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint8_t *xq,
+                              const float *sx, const int32_t *sorted_pairs,
+                              const int32_t *expert_offsets, const moe_weights *w, float *h,
+                              void *stream) {
+  const char *fn = "moe_expert_gate_up";
+  moe_status s = check_stage(dims, capacity, w, sorted_pairs, expert_offsets, fn);
+  if (s) return s;
+  if (!xq || !sx || !h) return fail(MOE_ERR_NULL, "%s: xq, sx and h are required", fn);
+  if (!aligned(xq, 16)) return fail(MOE_ERR_ALIGN, "%s: xq must be 16-byte aligned", fn);
+  RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
+  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, choose_msub(dims), as_stream(stream)), fn);
+  return s ? s : ok();
+}
+
+moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t *hq,
+                           const float *sh, const float *h, const int32_t *sorted_pairs,
+                           const int32_t *expert_offsets, const moe_weights *w, float *y,
+                           void *stream) {
+  const char *fn = "moe_expert_down";
+  moe_status s = check_stage(dims, capacity, w, sorted_pairs, expert_offsets, fn);
+  if (s) return s;
+  const bool f32 = dims->flags & MOE_F_NO_REQUANT;
+  if (!y) return fail(MOE_ERR_NULL, "%s: y is required", fn);
+  if (f32 ? !h : (!hq || !sh))
+    return fail(MOE_ERR_NULL, "%s: %s required", fn, f32 ? "h is" : "hq and sh are");
+  if ((f32 && !aligned(h, 16)) || (!f32 && !aligned(hq, 16)))
+    return fail(MOE_ERR_ALIGN, "%s: the activation rows must be 16-byte aligned", fn);
+  RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
+  s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
+                             choose_msub(dims), as_stream(stream)),
+                 fn);
+  return s ? s : ok();
+}
+
+moe_status moe_combine(const moe_dims *dims, int32_t capacity, const float *y,
+                       const int32_t *topk_ids, const float *topk_w, const int32_t *inv_pairs,
+                       float *out, void *stream) {
+  const char *fn = "moe_combine";
+  moe_status s = check_dims(dims, fn);
+  if (s) return s;
+  if (!y || !topk_ids || !topk_w || !inv_pairs || !out)
+    return fail(MOE_ERR_NULL, "%s: y, topk_ids, topk_w, inv_pairs and out are required", fn);
+  if (!aligned(y, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_ALIGN, "%s: y and out must be 16-byte aligned", fn);
+  if ((int64_t)capacity < capacity_of(dims->T, dims->E, dims->k_max, dims->block_m))
+    return fail(MOE_ERR_SHAPE, "%s: capacity=%d too small", fn, capacity);
+  RowSpace rs = row_space(dims, capacity, nullptr, nullptr);
+  s = hip_status(launch_combine(rs, y, topk_ids, topk_w, inv_pairs, out, as_stream(stream)), fn);
+  return s ? s : ok();
+}
+
+size_t moe_workspace_bytes(const moe_dims *dims) {
+  if (check_dims(dims, "moe_workspace_bytes")) return 0;
+  return layout_of(dims).total;
+}
+
+moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *w_router,
+                             const float *router_bias, const int32_t *k_per_token,
+                             const moe_weights *w, const float *logits_override, float *out,
+                             int32_t *topk_ids_out, float *topk_w_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  const char *fn = "moe_fused_forward";
+  moe_status s = check_dims(dims, fn);
+  if (s) return s;
+  if ((s = check_weights(dims, w, fn))) return s;
+  if (!x || !out) return fail(MOE_ERR_NULL, "%s: x and out are required", fn);
+  if (!w_router && !logits_override)
+    return fail(MOE_ERR_NULL, "%s: w_router is required unless logits_override is given", fn);
+  if (!aligned(x, 16) || !aligned(out, 16) || (w_router && !aligned(w_router, 16)))
+    return fail(MOE_ERR_ALIGN, "%s: x, out and w_router must be 16-byte aligned", fn);
+  const Layout L = layout_of(dims);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  if (!aligned(workspace, 256))
+    return fail(MOE_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+
+  hipStream_t st = as_stream(stream);
+  char *ws = static_cast<char *>(workspace);
+  uint8_t *xq = reinterpret_cast<uint8_t *>(ws + L.xq);
+  float *sx = reinterpret_cast<float *>(ws + L.sx);
+  float *logits = reinterpret_cast<float *>(ws + L.logits);
+  int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(ws + L.ids);
+  float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(ws + L.w);
+  int32_t *sorted = reinterpret_cast<int32_t *>(ws + L.sorted);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  int32_t *block_expert = reinterpret_cast<int32_t *>(ws + L.block_expert);
+  int32_t *inv = reinterpret_cast<int32_t *>(ws + L.inv);
+  int32_t *n_blocks = reinterpret_cast<int32_t *>(ws + L.n_blocks);
+  WorkItem *items = reinterpret_cast<WorkItem *>(ws + L.items);
+  int32_t *n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
+  float *h = reinterpret_cast<float *>(ws + L.h);
+  uint8_t *hq = reinterpret_cast<uint8_t *>(ws + L.hq);
+  float *sh = reinterpret_cast<float *>(ws + L.sh);
+  float *y = reinterpret_cast<float *>(ws + L.y);
+  const bool requant = !(dims->flags & MOE_F_NO_REQUANT);
+  hipEvent_t const *ev = g_stage_events;
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], st);
+  };
+
+  mark(0);
+  if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) return s;
+  mark(1);
+  const float *lg = logits_override;
+  if (!lg) {
+    if ((s = hip_status(launch_router(x, w_router, router_bias, dims->T, dims->d, dims->E, logits, st),
+                        "router")))
+      return s;
+    lg = logits;
+  }
+  mark(2);
+  if ((s = hip_status(launch_topk(lg, dims->T, dims->E, dims->k_max, k_per_token, ids, tw, st), "topk")))
+    return s;
+  mark(3);
+  if ((s = hip_status(launch_permute(ids, dims->T, dims->E, dims->k_max, dims->block_m, L.capacity,
+                                     sorted, offsets, block_expert, inv, n_blocks, items, n_items,
+                                     L.row_chunk, dims->n_shared, st),
+                      "permute")))
+    return s;
+  RowSpace rs = row_space(dims, L.capacity, sorted, offsets);
+  rs.items = items;
+  rs.n_items = n_items;
+  rs.max_items = L.max_items;
+  const ExpertWeights ew = to_internal(w);
+  mark(4);
+  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, st), "gate_up"))) return s;
+  mark(5);
+  if (requant) {
+    if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
+    mark(6);
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, st), "down"))) return s;
+  } else {
+    mark(6);
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, st), "down"))) return s;
+  }
+  mark(7);
+  if ((s = hip_status(launch_combine(rs, y, ids, tw, inv, out, st), "combine"))) return s;
+  mark(8);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of the FP8 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 512;  // routed experts per layer (top-k keys, permutation LDS)
+constexpr int kMaxK = 32;         // slots per token
+constexpr float kE4m3Max = 448.0f;
+
+// ---------------------------------------------------------------- e4m3 codec
+// gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round-to-nearest-even.
+// Inputs are clamped to +-448 first, which is the saturating rule for every
+// finite input (NaN inputs are outside the library's preconditions).
+__device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -kE4m3Max), kE4m3Max); }
+
+// Four floats -> four e4m3 codes packed little-endian in one 32-bit word.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+// Two e4m3 codes (bytes 0,1 or, with HI, bytes 2,3 of a word) -> two floats, exact.
+template <bool HI>
+__device__ __forceinline__ v2f e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// ---------------------------------------------------------------- MFMA
+// D = A * B^T + C on a 16x16 fp32 tile with K = 128 e4m3 values.
+// Lane l supplies row (l % 16) of A and row (l % 16) of B (B given with K
+// contiguous, i.e. as the N x K weight matrix), 32 bytes of K each; the same
+// K bytes must be supplied for A and B in the same lane.  Result: lane l,
+// element i holds C[4 * (l / 16) + i][l % 16].
+__device__ __forceinline__ v4f mfma_e4m3_16x16x128(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Same tile shape on fp16 operands with K = 32 (8 halves per lane).
+__device__ __forceinline__ v4f mfma_f16_16x16x32(v8h a, v8h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- row quantisation
+// One wave per row.  amax over the row, r = 448/amax and s = amax/448 as two
+// correctly rounded fp32 divisions, codes = e4m3(x * r).  The same IEEE
+// operations as the plain definition, so codes and scales are bit-exact.
+__device__ __forceinline__ void quantize_row_wave(const float *__restrict__ x, int cols,
+                                                  uint8_t *__restrict__ q, float *scale,
+                                                  int lane) {
+  float amax = 0.0f;
+  for (int i = lane * 4; i < cols; i += kWave * 4) {
+    v4f v = *reinterpret_cast<const v4f *>(x + i);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  amax = wave_max(amax);
+  float r = 1.0f, s = 1.0f;
+  if (amax != 0.0f) {
+    r = kE4m3Max / amax;
+    s = amax / kE4m3Max;
+  }
+  for (int i = lane * 4; i < cols; i += kWave * 4) {
+    v4f v = *reinterpret_cast<const v4f *>(x + i);
+    *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x * r, v.y * r, v.z * r, v.w * r);
+  }
+  if (lane == 0) *scale = s;
+}
+
+// ---------------------------------------------------------------- memory
+__device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
+
+__device__ __forceinline__ v4i load16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
+}  // namespace fp8moe

@@ -1,0 +1,66 @@
+// internal.hpp -- launch interface between the C ABI layer and the gfx950 kernels.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8moe {
+
+// One unit of grouped-GEMM work: `rows` consecutive expert rows starting at
+// `row0` of the expert-rows layout, all belonging to `expert` (e >= E means
+// shared expert e - E).
+struct WorkItem {
+  int32_t expert;
+  int32_t row0;
+  int32_t rows;
+  int32_t pad;
+};
+
+struct ExpertWeights {
+  const uint8_t *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;
+  const uint8_t *ws_gate, *ws_up, *ws_down;
+  const float *ss_gate, *ss_up, *ss_down;
+};
+
+// Shape of the expert-row space shared by the expert stages.
+struct RowSpace {
+  int32_t T, d, f, E, S, k_max;
+  int32_t capacity;      // routed rows (padded); shared rows follow
+  const int32_t *sorted_pairs;    // [capacity]
+  const int32_t *expert_offsets;  // [E+1]
+  const WorkItem *items;          // nullable: one item per expert, all its rows
+  const int32_t *n_items;         // device count of valid items (with items)
+  int32_t max_items;              // grid bound (with items)
+};
+
+hipError_t launch_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t *q,
+                                float *scale, hipStream_t stream);
+hipError_t launch_router(const float *x, const float *w_router, const float *bias, int32_t T,
+                         int32_t d, int32_t E, float *logits, hipStream_t stream);
+hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
+                       const int32_t *k_per_token, int32_t *ids, float *w, hipStream_t stream);
+// items/n_items/row_chunk: optional work list for the expert stages (row_chunk
+// rows per item); pass items == nullptr to skip it.
+hipError_t launch_permute(const int32_t *ids, int32_t T, int32_t E, int32_t k_max, int32_t block_m,
+                          int32_t capacity, int32_t *sorted_pairs, int32_t *expert_offsets,
+                          int32_t *block_expert, int32_t *inv_pairs, int32_t *n_blocks,
+                          WorkItem *items, int32_t *n_items, int32_t row_chunk, int32_t n_shared,
+                          hipStream_t stream);
+int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int32_t n_shared,
+                       int32_t row_chunk);
+
+hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
+                          const ExpertWeights &w, float *h, int32_t msub, hipStream_t stream);
+// Per-row e4m3 requantisation of h (real rows only): hq codes, sh = amax/448.
+hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
+                          hipStream_t stream);
+// Down projection from hq/sh, or (h32 != nullptr) straight from fp32 h with
+// fp32 products.
+hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
+                       const ExpertWeights &w, float *y, int32_t msub, hipStream_t stream);
+hipError_t launch_combine(const RowSpace &rs, const float *y, const int32_t *ids, const float *w,
+                          const int32_t *inv_pairs, float *out, hipStream_t stream);
+
+}  // namespace fp8moe

@@ -1,0 +1,225 @@
+/*
+ * fp8moe.h -- C ABI of the MI355X (gfx950) W8A8 FP8 Mixture-of-Experts layer.
+ *
+ * The layer, stated in the blog post "Routage MoE entre GPU": a router reads
+ * each token's hidden state and scores every expert, keeps the best k and
+ * gives each pick a routing weight; only the picked experts (each a
+ * feed-forward network with its own weights) process the token; their
+ * outputs are multiplied by the routing weights, summed, and put back in the
+ * original token order.  Weights and activations are 8-bit FP8 (W8A8; the
+ * Alpha-MoE article, opening section), and the article's section
+ * "Comment fonctionne le megakernel" names the stages fused here: routing,
+ * gating, expert compute and output combine.
+ *
+ * Readings taken where the pages are silent (each is a fixed convention of
+ * this library):
+ *   - FP8 is OCP E4M3FN (bias 7, largest finite 448, no infinities),
+ *     round to nearest, ties to even, saturating to +-448.
+ *   - Activations: one fp32 scale per token row, s = amax/448; the codes are
+ *     e4m3(x * fl(448/amax)); an all-zero row uses s = 1.
+ *   - Weights: one fp32 scale per output channel (per row of W_gate, W_up
+ *     [f][d] over d; per row of W_down [d][f] over f).
+ *   - Router: fp32 logits on the unquantised x, plus an optional bias.
+ *   - Top-k: experts ordered by (logit descending, index ascending), -0 and
+ *     +0 equal; weights are the softmax over the k selected logits.
+ *   - Expert: h = SiLU(g) * u with g, u the dequantised gate/up products;
+ *     h is requantised to e4m3 with one scale per (token, expert) row unless
+ *     MOE_F_NO_REQUANT is set; y = down projection of h.
+ *   - Combine: out[t] = sum_j w[t,j] * y(t, ids[t,j]) + sum_s y_shared(s,t);
+ *     shared experts have weight 1 and sit outside the softmax.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer; the library keeps no pointer after returning, never
+ *     allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; device-side faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failing call returns a non-zero moe_status, enqueues nothing, and
+ *     moe_last_error() describes the failure (thread-local text).
+ *   - Preconditions NOT checked on the device: inputs are finite, every
+ *     k_per_token[t] is in [1, k_max], every topk_ids entry is -1 or in [0, E).
+ *   - Calls on one stream are ordered; calls on different streams that share
+ *     output or workspace buffers race.
+ */
+#ifndef FP8MOE_H
+#define FP8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8MOE_ABI_VERSION 1
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is out of the supported range */
+  MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_UNSUPPORTED = 4, /* a flag or configuration this build does not run */
+  MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+};
+
+enum {
+  MOE_F_NO_REQUANT = 1u << 0 /* keep SiLU*up in fp32 and run the down projection on fp32
+                                products; an accuracy mode, not a fast path */
+};
+
+/* Limits checked by every call. */
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_K 32
+#define MOE_MAX_HIDDEN 16384 /* d: the router keeps a token's row in 64 KB of LDS */
+
+typedef struct {
+  int32_t T;        /* tokens, >= 1 */
+  int32_t d;        /* hidden size, multiple of 64, at most MOE_MAX_HIDDEN */
+  int32_t f;        /* expert intermediate size, multiple of 64 */
+  int32_t E;        /* routed experts, 1..512 */
+  int32_t k_max;    /* slots per token, 1..min(E, 32) */
+  int32_t n_shared; /* always-on shared experts, >= 0 */
+  int32_t block_m;  /* expert segments padded to a multiple of this: 1, 16, 32, 64 or 128 */
+  uint32_t flags;   /* MOE_F_* */
+} moe_dims;
+
+/* Expert weights: e4m3 codes (one byte each) and fp32 per-output-channel scales. */
+typedef struct {
+  const uint8_t *w_gate, *w_up; /* [E][f][d] row-major (d contiguous) */
+  const float *s_gate, *s_up;   /* [E][f] */
+  const uint8_t *w_down;        /* [E][d][f] row-major (f contiguous) */
+  const float *s_down;          /* [E][d] */
+  const uint8_t *ws_gate, *ws_up, *ws_down; /* shared experts: same layouts with */
+  const float *ss_gate, *ss_up, *ss_down;   /* n_shared in place of E; NULL when 0 */
+} moe_weights;
+
+/* ------------------------------------------------------------------------ */
+/* Single steps                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Per-row e4m3 quantisation (the W8A8 activation / weight encoding).
+ * x [rows][cols] fp32 -> q [rows][cols] e4m3 codes, scale [rows] fp32 with
+ * x ~= dec(q) * scale.  Used for per-token activations and, on weight
+ * matrices, for per-output-channel weight scales.
+ * cols: multiple of 4; x 16-byte aligned; q 4-byte aligned. */
+moe_status moe_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t *q, float *scale,
+                             void *stream);
+
+/* Router scores ("Routage MoE entre GPU", the router paragraph):
+ * logits[t][e] = sum_i x[t][i] * w_router[e][i] (+ bias[e]), fp32.
+ * x [T][d], w_router [E][d], bias [E] or NULL, logits [T][E]. */
+moe_status moe_router_logits(const float *x, const float *w_router, const float *bias, int32_t T,
+                             int32_t d, int32_t E, float *logits, void *stream);
+
+/* Top-k selection with routing weights (same paragraph: the router keeps the
+ * best experts and emits one weight per pick).  For token t with
+ * k_t = k_per_token ? k_per_token[t] : k_max: topk_ids[t][0..k_t) are the
+ * first k_t experts in (logit desc, index asc) order and topk_w the softmax of
+ * their logits; slots k_t..k_max-1 get id -1 and weight 0.
+ * logits [T][E], k_per_token [T] or NULL, topk_ids/topk_w [T][k_max]. */
+moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
+                          const int32_t *k_per_token, int32_t *topk_ids, float *topk_w,
+                          void *stream);
+
+/* Rows a permutation needs: T*k_max + E*(block_m-1). */
+int64_t moe_capacity(int32_t T, int32_t E, int32_t k_max, int32_t block_m);
+
+/* Dispatch on one device (the activation movement of "Routage MoE entre GPU"
+ * becomes a grouping of (token, slot) pairs by expert; the inverse map is
+ * what restores token order at the end).  Pair p = t*k_max + j is valid when
+ * topk_ids[p] >= 0.  Expert e's segment starts at
+ * expert_offsets[e] = sum_{e'<e} ceil(cnt[e']/block_m)*block_m and holds its
+ * pairs in ascending p, then the sentinel T*k_max; rows past the last segment
+ * also hold the sentinel.  block_expert[b] is the expert owning rows
+ * [b*block_m, (b+1)*block_m), -1 past the last segment.  inv_pairs[p] is p's
+ * row, -1 for an invalid pair.  n_blocks[0] = expert_offsets[E] / block_m.
+ * Deterministic: the result is unique.
+ * sorted_pairs [capacity], expert_offsets [E+1], block_expert
+ * [ceil(capacity/block_m)], inv_pairs [T*k_max], n_blocks [1]. */
+moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
+                       int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
+                       int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
+                       int32_t *n_blocks, void *stream);
+
+/* "Expert rows" layout used by the three expert stages below: rows
+ * [0, capacity) follow sorted_pairs (padding rows hold garbage or zeros);
+ * row capacity + s*T + t is token t for shared expert s.
+ * rows_total = capacity + n_shared*T. */
+
+/* Gate/up grouped GEMM with the SwiGLU epilogue, for every expert row:
+ *   g[o] = (sum_i dec(xq[t][i]) * dec(w_gate[e][o][i])) * sx[t] * s_gate[e][o]
+ *   u[o] likewise with w_up;  h[row][o] = SiLU(g[o]) * u[o]   (fp32)
+ * dims->flags is ignored.  xq [T][d], sx [T], h [rows_total][f]. */
+moe_status moe_expert_gate_up(const moe_dims *dims /*host*/, int32_t capacity, const uint8_t *xq,
+                              const float *sx, const int32_t *sorted_pairs,
+                              const int32_t *expert_offsets, const moe_weights *w /*host*/,
+                              float *h, void *stream);
+
+/* Down-projection grouped GEMM for every expert row:
+ *   y[row][c] = (sum_o dec(hq[row][o]) * dec(w_down[e][c][o])) * sh[row] * s_down[e][c]
+ * hq [rows_total][f] e4m3, sh [rows_total], y [rows_total][d] fp32.
+ * With MOE_F_NO_REQUANT in dims->flags the input is instead h [rows_total][f]
+ * fp32 (hq, sh ignored, may be NULL):
+ *   y[row][c] = (sum_o h[row][o] * dec(w_down[e][c][o])) * s_down[e][c]. */
+moe_status moe_expert_down(const moe_dims *dims /*host*/, int32_t capacity, const uint8_t *hq,
+                           const float *sh, const float *h, const int32_t *sorted_pairs,
+                           const int32_t *expert_offsets, const moe_weights *w /*host*/, float *y,
+                           void *stream);
+
+/* Weighted combine back into token order ("Routage MoE entre GPU", the last
+ * step):  out[t] = sum over valid j ascending of topk_w[t][j] * y[inv_pairs[t*k_max+j]]
+ *                  + sum over s ascending of y[capacity + s*T + t].
+ * y [rows_total][d], out [T][d]. */
+moe_status moe_combine(const moe_dims *dims /*host*/, int32_t capacity, const float *y,
+                       const int32_t *topk_ids, const float *topk_w, const int32_t *inv_pairs,
+                       float *out, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The whole layer                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace moe_fused_forward needs for these dims. */
+size_t moe_workspace_bytes(const moe_dims *dims /*host*/);
+
+/* Forward pass of one W8A8 FP8 MoE layer: quantise x, router logits (or
+ * logits_override), top-k + weights, permutation, gate/up + SiLU*up,
+ * requantisation, down projection, weighted combine.
+ * x [T][d] fp32; w_router [E][d] (may be NULL when logits_override is given);
+ * router_bias [E] or NULL; k_per_token [T] or NULL (all k_max);
+ * logits_override [T][E] or NULL; out [T][d] fp32;
+ * topk_ids_out / topk_w_out [T][k_max] or NULL;
+ * workspace: device buffer of at least moe_workspace_bytes(dims), 256-byte
+ * aligned, not touched by anything else while the work is in flight. */
+moe_status moe_fused_forward(const moe_dims *dims /*host*/, const float *x, const float *w_router,
+                             const float *router_bias, const int32_t *k_per_token,
+                             const moe_weights *w /*host*/, const float *logits_override,
+                             float *out, int32_t *topk_ids_out, float *topk_w_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Stage timing (instrumentation, not part of the layer).  After this call,
+ * moe_fused_forward on the calling thread records events[i] on its stream
+ * just before stage i (0 quantise, 1 router, 2 top-k, 3 permutation,
+ * 4 gate/up, 5 requantisation, 6 down, 7 combine) and events[8] after the
+ * last one.  `events` is a host array of MOE_N_STAGE_EVENTS hipEvent_t
+ * handles created and owned by the caller; the library keeps the pointer
+ * until the next call.  Pass NULL, 0 to stop.  Returns MOE_ERR_SHAPE when
+ * 0 < n_events < MOE_N_STAGE_EVENTS. */
+#define MOE_N_STAGE_EVENTS 9
+moe_status moe_debug_stage_events(void *const *events /*host*/, int32_t n_events);
+
+const char *moe_status_str(moe_status s);
+const char *moe_last_error(void); /* thread-local detail of this thread's last failing call */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8MOE_H */

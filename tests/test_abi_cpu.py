@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the HIP library loads, exports every entry
+point declared in include/fp8moe.h, and rejects bad arguments on the host
+before anything is enqueued (each call below fails validation, so no kernel
+is ever launched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8moe.h")
+
+fp8 = pytest.importorskip("fp8_moe_layer_amd", reason="libfp8moe.so not built")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(7)
+FAKE = 0x10000  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 13
+    lib = C.CDLL(str(fp8.LIB_PATH))
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings():
+    assert fp8.ABI_VERSION == 1
+    assert fp8._status_str(0) == b"ok"
+    assert fp8._status_str(ERR_WORKSPACE) == b"workspace too small"
+    assert fp8._status_str(99) == b"unknown status"
+
+
+def test_capacity_formula():
+    assert fp8.capacity(16, 8, 2, 16) == 16 * 2 + 8 * 15
+    assert fp8.capacity(1024, 512, 32, 1) == 1024 * 32
+
+
+def _dims(**kw):
+    base = dict(T=16, d=256, f=512, E=8, k_max=2, n_shared=0, block_m=16, no_requant=False)
+    base.update(kw)
+    return fp8.dims(**base)
+
+
+def test_workspace_bytes():
+    small = fp8.workspace_bytes(_dims(T=16))
+    big = fp8.workspace_bytes(_dims(T=1024))
+    assert 0 < small < big
+    assert fp8.workspace_bytes(_dims(T=0)) == 0           # invalid dims -> 0
+    assert fp8.workspace_bytes(_dims(block_m=7)) == 0
+    # Mixtral-shaped decode layer fits comfortably
+    mix = fp8.workspace_bytes(_dims(T=256, d=4096, f=14336, E=8, k_max=2))
+    assert mix < 512 << 20
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), ERR_SHAPE),
+    (dict(d=100), ERR_SHAPE),
+    (dict(f=96), ERR_SHAPE),
+    (dict(E=0), ERR_SHAPE),
+    (dict(E=513, k_max=2), ERR_SHAPE),
+    (dict(k_max=9), ERR_SHAPE),
+    (dict(E=64, k_max=33), ERR_SHAPE),
+    (dict(block_m=24), ERR_SHAPE),
+    (dict(n_shared=-1), ERR_SHAPE),
+])
+def test_fused_forward_rejects_bad_dims(kw, code):
+    dm = _dims(**kw)
+    w = fp8._Weights(*([FAKE] * 12))
+    rc = fp8._fused_forward(C.byref(dm), FAKE, FAKE, None, None, C.byref(w), None, FAKE, None, None,
+                            FAKE, 1 << 40, None)
+    assert rc == code, fp8._last_error()
+    assert fp8._last_error()
+
+
+def test_fused_forward_rejects_null_and_alignment_and_workspace():
+    dm = _dims()
+    w = fp8._Weights(*([FAKE] * 12))
+    call = lambda **kw: fp8._fused_forward(
+        C.byref(kw.get("dims", dm)), kw.get("x", FAKE), kw.get("wr", FAKE), None, None,
+        C.byref(kw.get("w", w)), kw.get("lo", None), kw.get("out", FAKE), None, None,
+        kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
+    assert fp8._fused_forward(None, FAKE, FAKE, None, None, C.byref(w), None, FAKE, None, None,
+                              FAKE, 1 << 40, None) == ERR_NULL
+    assert call(x=None) == ERR_NULL
+    assert call(wr=None) == ERR_NULL                       # no router and no override
+    assert call(x=FAKE + 4) == ERR_ALIGN
+    assert call(ws=FAKE + 16) == ERR_ALIGN
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(wsb=fp8.workspace_bytes(dm) - 1) == ERR_WORKSPACE
+    w2 = fp8._Weights(*([FAKE] * 12))
+    w2.w_down = None
+    assert call(w=w2) == ERR_NULL
+    w3 = fp8._Weights(*([FAKE] * 12))
+    w3.w_gate = FAKE + 8
+    assert call(w=w3) == ERR_ALIGN
+    sh = _dims(n_shared=2)
+    w4 = fp8._Weights(*([FAKE] * 6 + [None] * 6))
+    assert call(dims=sh, w=w4) == ERR_NULL
+    bad_flags = _dims()
+    bad_flags.flags = 1 << 5
+    assert call(dims=bad_flags) == ERR_UNSUPPORTED
+
+
+def test_step_entry_points_reject_bad_arguments():
+    assert fp8._quantize_rows(None, 4, 8, FAKE, FAKE, None) == ERR_NULL
+    assert fp8._quantize_rows(FAKE, 4, 6, FAKE, FAKE, None) == ERR_SHAPE
+    assert fp8._quantize_rows(FAKE + 4, 4, 8, FAKE, FAKE, None) == ERR_ALIGN
+    assert fp8._router_logits(FAKE, FAKE, None, 4, 100, 8, FAKE, None) == ERR_SHAPE
+    assert fp8._router_logits(FAKE, None, None, 4, 128, 8, FAKE, None) == ERR_NULL
+    assert fp8._route_topk(FAKE, 4, 8, 9, None, FAKE, FAKE, None) == ERR_SHAPE
+    assert fp8._route_topk(FAKE, 4, 600, 2, None, FAKE, FAKE, None) == ERR_SHAPE
+    assert fp8._route_topk(FAKE, 4, 64, 33, None, FAKE, FAKE, None) == ERR_SHAPE
+    assert fp8._permute(FAKE, 4, 8, 2, 16, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert fp8._permute(FAKE, 4, 8, 2, 3, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert fp8._permute(FAKE, 4, 8, 2, 16, 1000, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_NULL
+    dm = _dims()
+    w = fp8._Weights(*([FAKE] * 12))
+    cap = fp8.capacity(16, 8, 2, 16)
+    assert fp8._gate_up(C.byref(dm), cap - 1, FAKE, FAKE, FAKE, FAKE, C.byref(w), FAKE, None) == ERR_SHAPE
+    assert fp8._gate_up(C.byref(dm), cap, None, FAKE, FAKE, FAKE, C.byref(w), FAKE, None) == ERR_NULL
+    assert fp8._down(C.byref(dm), cap, None, FAKE, None, FAKE, FAKE, C.byref(w), FAKE, None) == ERR_NULL
+    nr = _dims(no_requant=True)
+    assert fp8._down(C.byref(nr), cap, FAKE, FAKE, None, FAKE, FAKE, C.byref(w), FAKE, None) == ERR_NULL
+    assert fp8._combine(C.byref(dm), cap, FAKE, FAKE, FAKE, None, FAKE, None) == ERR_NULL
+    assert fp8._combine(C.byref(dm), 3, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert b"capacity" in fp8._last_error()
