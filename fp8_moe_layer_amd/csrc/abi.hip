@@ -46,7 +46,8 @@ moe_status check_dims(const moe_dims *d, const char *fn) {
   if (d->T < 1) return fail(MOE_ERR_SHAPE, "%s: T=%d must be >= 1", fn, d->T);
   if (d->d < 64 || d->d % 64 || d->d > MOE_MAX_HIDDEN)
     return fail(MOE_ERR_SHAPE, "%s: d=%d must be a multiple of 64 in [64, %d]", fn, d->d, MOE_MAX_HIDDEN);
-  if (d->f < 64 || d->f % 64) return fail(MOE_ERR_SHAPE, "%s: f=%d must be a positive multiple of 64", fn, d->f);
+  if (d->f < 64 || d->f % 64 || d->f > MOE_MAX_FFN)
+    return fail(MOE_ERR_SHAPE, "%s: f=%d must be a multiple of 64 in [64, %d]", fn, d->f, MOE_MAX_FFN);
   if (d->E < 1 || d->E > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_SHAPE, "%s: E=%d must be in [1, %d]", fn, d->E, MOE_MAX_EXPERTS);
   if (d->k_max < 1 || d->k_max > d->E || d->k_max > MOE_MAX_K)
@@ -101,11 +102,24 @@ int32_t choose_msub(const moe_dims *d) {
   return m;
 }
 
+// K splits of the down projection: enough workgroups to keep every CU
+// streaming when few experts are active (decode), one split otherwise.
+int32_t choose_down_splits(const moe_dims *d, int32_t msub) {
+  if (d->flags & MOE_F_NO_REQUANT) return 1;
+  const double E = d->E;
+  const double active = E * (1.0 - pow(1.0 - (double)d->k_max / E, (double)d->T)) + d->n_shared;
+  const double tiles = (d->d + 63) / 64;
+  int32_t s = (int32_t)ceil(1024.0 / (active * tiles));
+  if (s < 1) s = 1;
+  if (s > 8) s = 8;
+  return down_splits_used(d->f, msub, s);
+}
+
 // Workspace layout of moe_fused_forward (all pieces 256-byte aligned).
 struct Layout {
   size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
       hq, sh, y, total;
-  int32_t capacity, rows_total, max_items, row_chunk, msub;
+  int32_t capacity, rows_total, max_items, row_chunk, msub, splits;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -116,6 +130,7 @@ Layout layout_of(const moe_dims *d) {
   L.rows_total = L.capacity + d->n_shared * d->T;
   L.msub = choose_msub(d);
   L.row_chunk = 16 * L.msub;
+  L.splits = choose_down_splits(d, L.msub);
   L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
   const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
   size_t o = 0;
@@ -139,7 +154,7 @@ Layout layout_of(const moe_dims *d) {
   L.h = take(R * d->f * 4);
   L.hq = take(R * d->f);
   L.sh = take(R * 4);
-  L.y = take(R * d->d * 4);
+  L.y = take((size_t)L.splits * R * d->d * 4);
   L.total = o;
   return L;
 }
@@ -298,7 +313,7 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
     return fail(MOE_ERR_ALIGN, "%s: the activation rows must be 16-byte aligned", fn);
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
-                             choose_msub(dims), as_stream(stream)),
+                             choose_msub(dims), 1, as_stream(stream)),
                  fn);
   return s ? s : ok();
 }
@@ -316,7 +331,7 @@ moe_status moe_combine(const moe_dims *dims, int32_t capacity, const float *y,
   if ((int64_t)capacity < capacity_of(dims->T, dims->E, dims->k_max, dims->block_m))
     return fail(MOE_ERR_SHAPE, "%s: capacity=%d too small", fn, capacity);
   RowSpace rs = row_space(dims, capacity, nullptr, nullptr);
-  s = hip_status(launch_combine(rs, y, topk_ids, topk_w, inv_pairs, out, as_stream(stream)), fn);
+  s = hip_status(launch_combine(rs, y, 1, topk_ids, topk_w, inv_pairs, out, as_stream(stream)), fn);
   return s ? s : ok();
 }
 
@@ -400,13 +415,14 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(6);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, st), "down"))) return s;
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, st), "down")))
+      return s;
   } else {
     mark(6);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, st), "down"))) return s;
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, st), "down"))) return s;
   }
   mark(7);
-  if ((s = hip_status(launch_combine(rs, y, ids, tw, inv, out, st), "combine"))) return s;
+  if ((s = hip_status(launch_combine(rs, y, L.splits, ids, tw, inv, out, st), "combine"))) return s;
   mark(8);
   return ok();
 }

@@ -57,10 +57,16 @@ hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream);
 // Down projection from hq/sh, or (h32 != nullptr) straight from fp32 h with
-// fp32 products.
+// fp32 products.  `splits` > 1 cuts K = f into that many ranges (fewer if f
+// is short) whose partial sums go to separate y slabs [split][rows][d]; the
+// count actually used is down_splits_used(f, msub, splits).
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
-                       const ExpertWeights &w, float *y, int32_t msub, hipStream_t stream);
-hipError_t launch_combine(const RowSpace &rs, const float *y, const int32_t *ids, const float *w,
-                          const int32_t *inv_pairs, float *out, hipStream_t stream);
+                       const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
+                       hipStream_t stream);
+int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
+// out from y slabs summed in split order.
+hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
+                          const float *w, const int32_t *inv_pairs, float *out,
+                          hipStream_t stream);
 
 }  // namespace fp8moe

@@ -7,17 +7,26 @@
 // weighted, summed and put back in token order.  W8A8 FP8: Alpha-MoE article,
 // opening section.
 //
-// Grouped GEMM schedule (weight-stationary).  A workgroup owns one work item
-// (an expert and up to a chunk of that expert's rows) and one tile of output
-// channels; it streams that tile's weight rows from HBM exactly once per pass
-// of up to 16*MSUB rows and multiplies them against every row of the pass.
-// Decode-sized batches fit all rows of an expert in one pass, so each active
-// expert's weights cross HBM once.  Each wave owns 16 output channels (two
-// weight rows per lane for gate/up, `kDownSub` row groups for down) and runs
-// v_mfma_f32_16x16x128_f8f6f4 on e4m3 operands read straight from global
-// memory into the MFMA lane layout: lane l supplies row l%16 and the 32
-// K-bytes [32*(l/16), 32*(l/16)+32) of every 128-wide K step, for both the
-// activation row and the weight row.
+// Grouped GEMM schedule: weight-stationary, one workgroup per (work item,
+// tile of output channels[, K split]).  A work item is an expert and up to
+// 16*MSUB of its rows, so a decode-sized batch puts all of an expert's rows
+// in one item and each active expert's weights cross HBM exactly once.
+//
+// Workgroup = 4 compute waves + 1 loader wave (320 lanes):
+//  - the loader wave gathers the item's activation rows (e4m3) into LDS with
+//    global_load_lds_dwordx4, 32 KB chunks of K, double buffered;
+//  - each compute wave streams its own weight rows (16 output channels; the
+//    gate and the up row of each for the gate/up GEMM) straight from HBM
+//    into registers through a PF-deep prefetch ring, reads the activation
+//    fragments from LDS and runs v_mfma_f32_16x16x128_f8f6f4;
+//  - one s_barrier per chunk hands buffers between them.  The barrier waits
+//    only on LDS counters, so the weight prefetches stay in flight across it.
+//
+// MFMA operand layout (same for A = activation rows and B = weight rows):
+// lane l holds row l%16 and, of each 128-byte K step, the bytes
+// [16*(l/16), +16) and [64 + 16*(l/16), +16).  Each 16-byte piece load of a
+// wave then covers 16 rows x 64 contiguous bytes.  Result tile: lane l,
+// element i = C[4*(l/16) + i][l%16].
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -31,14 +40,10 @@ struct GemmArgs {
   const float *a_scale;  // sx [T] or sh [rows]
   const float *a32;      // down, fp32 mode: h [rows][f]
   ExpertWeights w;
-  float *out;            // h [rows][f] or y [rows][d]
+  float *out;            // h [rows][f] or y [splits][rows][d]
+  int32_t splits;        // K splits (down only; partial sums go to separate y slabs)
+  int32_t ksplit;        // bytes of K per split (multiple of the chunk size)
 };
-
-__device__ __forceinline__ v8i load32(const uint8_t *p) {
-  const v4i lo = *reinterpret_cast<const v4i *>(p);
-  const v4i hi = *reinterpret_cast<const v4i *>(p + 16);
-  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
 
 __device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, int &expert,
                                              int &row0, int &rows) {
@@ -72,84 +77,233 @@ __device__ __forceinline__ bool row_real(const RowSpace &rs, int grow) {
   return grow >= rs.capacity || rs.sorted_pairs[grow] < rs.T * rs.k_max;
 }
 
-constexpr v8i kZero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
+// its outstanding global loads.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Loader side: its direct-to-LDS loads are counted by vmcnt.
+__device__ __forceinline__ void barrier_after_loads() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
 
 }  // namespace
 
-// ------------------------------------------------------------------ gate/up
-// h[row][o] = SiLU(g) * u with g = (G * sx[t]) * s_gate[o], u likewise, and
-// G, U the e4m3 products accumulated in fp32 by the MFMA.
+// 64 zero bytes: the source of activation pieces for padding rows and K
+// past the end.  Never written.
+__device__ __attribute__((aligned(64))) uint8_t g_zero_piece[64];
+
+// ------------------------------------------------------------------ grouped GEMM
+
 template <int MSUB>
-__global__ __launch_bounds__(256) void gate_up_kernel(GemmArgs g) {
+struct Chunk {
+  static constexpr int MP = 16 * MSUB;        // rows per pass
+  static constexpr int KC = 32768 / MP;       // K bytes per LDS chunk
+  static constexpr int KSC = KC / 128;        // K steps per chunk
+  static constexpr int BYTES = MSUB * KSC * 2048;
+  // weight prefetch depth in k steps (deeper for the single-subtile case,
+  // which has the fewest MFMAs per byte and the registers to spare)
+  static constexpr int PF = MSUB == 1 ? 4 : 2;
+};
+
+// GATEUP: out = h[rows][f], NB must be 2 (gate row, up row of the same channel).
+// else:   out = y[split][rows][d], NB channel groups of 16 per wave.
+template <int MSUB, int NB, bool GATEUP>
+__global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
+  using C = Chunk<MSUB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[2][C::BYTES];
+
   const RowSpace &rs = g.rs;
-  const int d = rs.d, f = rs.f;
-  const int n_tiles = f >> 6;
-  const int item_id = blockIdx.x / n_tiles;
-  const int tile = blockIdx.x - item_id * n_tiles;
+  const int K = GATEUP ? rs.d : rs.f;
+  const int N = GATEUP ? rs.f : rs.d;
+  constexpr int CH_WAVE = GATEUP ? 16 : 16 * NB;
+  constexpr int CH_WG = 4 * CH_WAVE;
+  const int n_tiles = (N + CH_WG - 1) / CH_WG;
+  int bid = blockIdx.x;
+  const int split = bid % g.splits;
+  bid /= g.splits;
+  const int tile = bid % n_tiles;
+  const int item_id = bid / n_tiles;
   int expert, row0, rows;
   if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  const int k_begin = split * g.ksplit;
+  const int k_end = min(K, k_begin + g.ksplit);
+  if (k_begin >= k_end) return;
+  const int nks = (k_end - k_begin + 127) >> 7;         // K steps in this split
+  // K steps are processed PF at a time; steps past nks multiply zero
+  // activation pieces by a repeat of the last weight step.
+  const int nks_pf = (nks + C::PF - 1) / C::PF * C::PF;
+  const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;
+  const bool half_tail = (k_end - k_begin) & 127;       // last step holds 64 bytes
+
   const bool shared = expert >= rs.E;
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
-  const uint8_t *wg = (shared ? g.w.ws_gate : g.w.w_gate) + ex * f * d;
-  const uint8_t *wu = (shared ? g.w.ws_up : g.w.w_up) + ex * f * d;
-  const float *sg = (shared ? g.w.ss_gate : g.w.s_gate) + ex * f;
-  const float *su = (shared ? g.w.ss_up : g.w.s_up) + ex * f;
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kg = lane >> 4;
-  const int o = (tile << 6) + (wave << 4) + ln;  // this lane's output channel
-  const uint8_t *bgp = wg + (size_t)o * d + kg * 32;
-  const uint8_t *bup = wu + (size_t)o * d + kg * 32;
-  const int nk = (d + 127) >> 7;
-  const bool half_tail = (d & 127) != 0;  // last K step holds 64 bytes: groups 2,3 idle
-  const float sgo = sg[o], suo = su[o];
 
-  for (int p0 = 0; p0 < rows; p0 += 16 * MSUB) {
-    const int msub = min(MSUB, (rows - p0 + 15) >> 4);
-    const uint8_t *ap[MSUB];
+  if (wave == 4) {
+    // ---------------- loader wave: activation rows -> LDS, chunk by chunk
+    const uint8_t *abase[MSUB];
+    for (int p0 = 0; p0 < rows; p0 += C::MP) {
+      const int prow = min(C::MP, rows - p0);
+      const int msub = (prow + 15) >> 4;
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      const int r = p0 + m * 16 + ln;
-      int tok = -1;
-      if (m < msub && r < rows) tok = row_token(rs, row0 + r);
-      ap[m] = tok >= 0 ? g.a + (size_t)tok * d + kg * 32 : nullptr;
+      for (int m = 0; m < MSUB; ++m) {
+        const int r = p0 + m * 16 + ln;
+        const uint8_t *b = nullptr;
+        if (m < msub && r < rows) {
+          if (GATEUP) {
+            const int tok = row_token(rs, row0 + r);
+            if (tok >= 0) b = g.a + (size_t)tok * K;
+          } else if (row_real(rs, row0 + r)) {
+            b = g.a + (size_t)(row0 + r) * K;
+          }
+        }
+        abase[m] = b;
+      }
+      auto load_chunk = [&](int c) {
+        uint8_t *dst = abuf[c & 1];
+        const int steps = min(C::KSC, nks_pf - c * C::KSC);
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m) {
+          if (m < msub) {
+            for (int s = 0; s < steps; ++s) {
+#pragma unroll
+              for (int p = 0; p < 2; ++p) {
+                const int kb = k_begin + (c * C::KSC + s) * 128 + p * 64 + kg * 16;
+                const uint8_t *src = (abase[m] && kb < k_end) ? abase[m] + kb : g_zero_piece;
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ((m * C::KSC + s) * 2 + p) * 1024),
+                                                 16, 0, 0);
+              }
+            }
+          }
+        }
+      };
+      load_chunk(0);
+      barrier_after_loads();
+      for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) load_chunk(c + 1);
+        barrier_after_loads();
+      }
     }
-    v4f accg[MSUB], accu[MSUB];
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m) accg[m] = accu[m] = v4f{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
 
-    for (int ks = 0; ks < nk; ++ks) {
-      const int k = ks << 7;
-      const bool kval = !(half_tail && ks == nk - 1 && kg >= 2);
-      const v8i bg = kval ? load32(bgp + k) : kZero8;
-      const v8i bu = kval ? load32(bup + k) : kZero8;
+  // ---------------- compute waves
+  const uint8_t *bw[NB];
+  int ch[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int o;
+    const uint8_t *wbase;
+    if (GATEUP) {
+      o = tile * CH_WG + wave * 16 + ln;
+      wbase = (nb == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
+              ex * (size_t)N * K;
+    } else {
+      o = tile * CH_WG + wave * CH_WAVE + nb * 16 + ln;
+      wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * K;
+    }
+    ch[nb] = o;
+    const int orow = o < N ? o : N - 1;  // a partial last tile re-reads a valid row
+    bw[nb] = wbase + (size_t)orow * K + k_begin + kg * 16;
+  }
+  // Weight pieces of k step ks: +ks*128 and +ks*128+64.  Past the end the step
+  // is clamped to the last one; in a 64-byte tail step the second piece
+  // repeats the first (its activation piece is zero).
+  auto load_b = [&](v8i (&b)[NB], int ks) {
+    ks = min(ks, nks - 1);
+    const int o0 = ks * 128;
+    const int o1 = (half_tail && ks == nks - 1) ? o0 : o0 + 64;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const v4i lo = load16(bw[nb] + o0);
+      const v4i hi = load16(bw[nb] + o1);
+      b[nb] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  };
+
+  v8i ring[C::PF][NB];
+  v4f acc[MSUB][NB];
+  const uint8_t *lds_lane = &abuf[0][0] + lane * 16;
+  for (int p0 = 0; p0 < rows; p0 += C::MP) {
+    const int prow = min(C::MP, rows - p0);
+    const int msub = (prow + 15) >> 4;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[m][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::PF; ++s) load_b(ring[s], s);
+    barrier_lds();
+
+    for (int ks0 = 0; ks0 < nks_pf; ks0 += C::PF) {
+#pragma unroll
+      for (int s = 0; s < C::PF; ++s) {
+        const int ks = ks0 + s;
+        const int c = ks / C::KSC;
+        const uint8_t *fa = lds_lane + (c & 1) * C::BYTES + (ks - c * C::KSC) * 2048;
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m) {
+          if (m < msub) {
+            const v4i a0 = *reinterpret_cast<const v4i *>(fa + m * C::KSC * 2048);
+            const v4i a1 = *reinterpret_cast<const v4i *>(fa + m * C::KSC * 2048 + 1024);
+            const v8i a = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[m][nb] = mfma_e4m3_16x16x128(a, ring[s][nb], acc[m][nb]);
+          }
+        }
+        load_b(ring[s], ks + C::PF);
+      }
+      const int next = ks0 + C::PF;
+      if (next % C::KSC == 0 || next == nks_pf) barrier_lds();
+    }
+
+    // ---------------- epilogue
+    if (GATEUP) {
+      const int o = ch[0];
+      const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + o];
+      const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + o];
 #pragma unroll
       for (int m = 0; m < MSUB; ++m) {
         if (m < msub) {
-          const v8i av = (ap[m] && kval) ? load32(ap[m] + k) : kZero8;
-          accg[m] = mfma_e4m3_16x16x128(av, bg, accg[m]);
-          accu[m] = mfma_e4m3_16x16x128(av, bu, accu[m]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = p0 + m * 16 + kg * 4 + i;
+            if (r < rows) {
+              const int grow = row0 + r;
+              const int tok = row_token(rs, grow);
+              float hv = 0.0f;
+              if (tok >= 0) {
+                const float sxt = g.a_scale[tok];
+                const float gv = acc[m][0][i] * sxt * sgo;
+                const float uv = acc[m][1][i] * sxt * suo;
+                hv = gv / (1.0f + expf(-gv)) * uv;
+              }
+              g.out[(size_t)grow * N + o] = hv;
+            }
+          }
         }
       }
-    }
-
+    } else {
+      const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * N;
+      float *ys = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N;
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      if (m < msub) {
+      for (int m = 0; m < MSUB; ++m) {
+        if (m < msub) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = p0 + m * 16 + kg * 4 + i;
-          if (r < rows) {
-            const int grow = row0 + r;
-            const int tok = row_token(rs, grow);
-            float hv = 0.0f;
-            if (tok >= 0) {
-              const float sxt = g.a_scale[tok];
-              const float gv = accg[m][i] * sxt * sgo;
-              const float uv = accu[m][i] * sxt * suo;
-              hv = gv / (1.0f + expf(-gv)) * uv;
+          for (int i = 0; i < 4; ++i) {
+            const int r = p0 + m * 16 + kg * 4 + i;
+            if (r < rows) {
+              const int grow = row0 + r;
+              const bool real = row_real(rs, grow);
+              const float shr = real ? g.a_scale[grow] : 0.0f;
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                if (ch[nb] < N) ys[(size_t)grow * N + ch[nb]] = real ? acc[m][nb][i] * shr * sd[ch[nb]] : 0.0f;
+              }
             }
-            g.out[(size_t)grow * f + o] = hv;
           }
         }
       }
@@ -157,29 +311,15 @@ __global__ __launch_bounds__(256) void gate_up_kernel(GemmArgs g) {
   }
 }
 
-// ------------------------------------------------------------------ requant
-// One wave per real expert row: hq = e4m3(h * 448/amax), sh = amax/448.
-__global__ __launch_bounds__(256) void requant_kernel(RowSpace rs, const float *__restrict__ h,
-                                                      uint8_t *__restrict__ hq,
-                                                      float *__restrict__ sh, int rows_total) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows_total || !row_real(rs, row)) return;
-  quantize_row_wave(h + (size_t)row * rs.f, rs.f, hq + (size_t)row * rs.f, sh + row,
-                    threadIdx.x & 63);
-}
-
-// ------------------------------------------------------------------ down
-// y[row][c] = (Y * sh[row]) * s_down[c], Y = sum_o dec(hq[row][o]) dec(Wd[c][o]).
-// F32A: y[row][c] = Y * s_down[c] with Y = sum_o h[row][o] dec(Wd[c][o]) on
-// fp32 products (v_mfma_f32_16x16x4_f32; instruction i of a 128-wide step
-// takes K index 32*(l/16) + i from lane l, for A and B alike).
-constexpr int kDownSub = 2;  // 16-channel groups per wave -> 128 channels per workgroup
-
-template <int MSUB, bool F32A>
-__global__ __launch_bounds__(256) void down_kernel(GemmArgs g) {
+// ------------------------------------------------------------------ down, fp32 products
+// No-requant mode: y[row][c] = (sum_o h[row][o] dec(Wd[c][o])) * s_down[c] on
+// v_mfma_f32_16x16x4_f32.  Instruction i of a 128-wide K step takes K index
+// 32*(l/16) + i from lane l, for A and B alike.  An accuracy mode: simple
+// direct loads, no prefetch pipeline.
+__global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
   const RowSpace &rs = g.rs;
   const int d = rs.d, f = rs.f;
-  const int n_tiles = (d + 127) >> 7;
+  const int n_tiles = (d + 63) >> 6;
   const int item_id = blockIdx.x / n_tiles;
   const int tile = blockIdx.x - item_id * n_tiles;
   int expert, row0, rows;
@@ -188,129 +328,115 @@ __global__ __launch_bounds__(256) void down_kernel(GemmArgs g) {
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
   const uint8_t *wd = (shared ? g.w.ws_down : g.w.w_down) + ex * d * f;
   const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * d;
-
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 15, kg = lane >> 4;
-  int oc[kDownSub];
-  const uint8_t *bp[kDownSub];
-#pragma unroll
-  for (int n = 0; n < kDownSub; ++n) {
-    oc[n] = (tile << 7) + (wave << 5) + (n << 4) + ln;
-    bp[n] = oc[n] < d ? wd + (size_t)oc[n] * f + kg * 32 : nullptr;
-  }
+  const int oc = (tile << 6) + (wave << 4) + ln;
+  const uint8_t *bp = wd + (size_t)(oc < d ? oc : d - 1) * f + kg * 32;
   const int nk = (f + 127) >> 7;
   const bool half_tail = (f & 127) != 0;
-
-  for (int p0 = 0; p0 < rows; p0 += 16 * MSUB) {
-    const int msub = min(MSUB, (rows - p0 + 15) >> 4);
-    size_t aoff[MSUB];
-    bool aok[MSUB];
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      const int r = p0 + m * 16 + ln;
-      aok[m] = m < msub && r < rows && row_real(rs, row0 + r);
-      aoff[m] = (size_t)(row0 + r) * f + kg * 32;
-    }
-    v4f acc[MSUB][kDownSub];
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-      for (int n = 0; n < kDownSub; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
-
+  for (int r0 = 0; r0 < rows; r0 += 16) {
+    const int r = r0 + ln;
+    const bool aok = r < rows && row_real(rs, row0 + r);
+    const float *arow = g.a32 + (size_t)(row0 + (r < rows ? r : 0)) * f + kg * 32;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
     for (int ks = 0; ks < nk; ++ks) {
       const int k = ks << 7;
       const bool kval = !(half_tail && ks == nk - 1 && kg >= 2);
-      v8i b[kDownSub];
+      v4i w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
+      if (kval) {
+        w0 = load16(bp + k);
+        w1 = load16(bp + k + 16);
+      }
+      const uint32_t ww[8] = {(uint32_t)w0.x, (uint32_t)w0.y, (uint32_t)w0.z, (uint32_t)w0.w,
+                              (uint32_t)w1.x, (uint32_t)w1.y, (uint32_t)w1.z, (uint32_t)w1.w};
 #pragma unroll
-      for (int n = 0; n < kDownSub; ++n) b[n] = (kval && bp[n]) ? load32(bp[n] + k) : kZero8;
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        if (m < msub) {
-          if constexpr (!F32A) {
-            const v8i av = (aok[m] && kval) ? load32(g.a + aoff[m] + k) : kZero8;
-#pragma unroll
-            for (int n = 0; n < kDownSub; ++n) acc[m][n] = mfma_e4m3_16x16x128(av, b[n], acc[m][n]);
-          } else {
-            float af[32];
-            const float *src = g.a32 + aoff[m] + k;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              v4f v = (aok[m] && kval) ? *reinterpret_cast<const v4f *>(src + 4 * q)
-                                       : v4f{0.f, 0.f, 0.f, 0.f};
-              af[4 * q] = v.x;
-              af[4 * q + 1] = v.y;
-              af[4 * q + 2] = v.z;
-              af[4 * q + 3] = v.w;
-            }
-#pragma unroll
-            for (int n = 0; n < kDownSub; ++n) {
-#pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                const uint32_t wword = (uint32_t)b[n][q];
-                const v2f lo = e4m3x2_to_f32<false>(wword);
-                const v2f hi = e4m3x2_to_f32<true>(wword);
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[4 * q], lo.x, acc[m][n], 0, 0, 0);
-                acc[m][n] =
-                    __builtin_amdgcn_mfma_f32_16x16x4f32(af[4 * q + 1], lo.y, acc[m][n], 0, 0, 0);
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[4 * q + 2], hi.x, acc[m][n], 0, 0, 0);
-                acc[m][n] =
-                    __builtin_amdgcn_mfma_f32_16x16x4f32(af[4 * q + 3], hi.y, acc[m][n], 0, 0, 0);
-              }
-            }
-          }
-        }
+      for (int q = 0; q < 8; ++q) {
+        v4f av = {0.f, 0.f, 0.f, 0.f};
+        if (aok && kval) av = *reinterpret_cast<const v4f *>(arow + k + 4 * q);
+        const v2f lo = e4m3x2_to_f32<false>(ww[q]);
+        const v2f hi = e4m3x2_to_f32<true>(ww[q]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, lo.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, lo.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, hi.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, hi.y, acc, 0, 0, 0);
       }
     }
-
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      if (m < msub) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = p0 + m * 16 + kg * 4 + i;
-          if (r < rows) {
-            const int grow = row0 + r;
-            const bool real = row_real(rs, grow);
-            const float shr = (!F32A && real) ? g.a_scale[grow] : 1.0f;
-#pragma unroll
-            for (int n = 0; n < kDownSub; ++n) {
-              if (oc[n] < d) {
-                float yv = 0.0f;
-                if (real) yv = F32A ? acc[m][n][i] * sd[oc[n]] : acc[m][n][i] * shr * sd[oc[n]];
-                g.out[(size_t)grow * d + oc[n]] = yv;
-              }
-            }
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int rr = r0 + kg * 4 + i;
+      if (rr < rows && oc < d) {
+        const int grow = row0 + rr;
+        g.out[(size_t)grow * d + oc] = row_real(rs, grow) ? acc[i] * sd[oc] : 0.0f;
       }
     }
   }
 }
 
+// ------------------------------------------------------------------ requant
+// One workgroup per real expert row: hq = e4m3(h * 448/amax), sh = amax/448,
+// the row held in registers between the max and the conversion.
+constexpr int kRowThreads = 256;
+constexpr int kRowVec = 16;  // float4 per thread: rows up to 16384 values
+
+__global__ __launch_bounds__(kRowThreads) void requant_kernel(RowSpace rs, const float *__restrict__ h,
+                                                              uint8_t *__restrict__ hq,
+                                                              float *__restrict__ sh) {
+  const int row = blockIdx.x;
+  if (!row_real(rs, row)) return;
+  __shared__ float red[kRowThreads / kWave];
+  const int f = rs.f;
+  const float *src = h + (size_t)row * f;
+  v4f v[kRowVec];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kRowVec; ++j) {
+    const int i = (j * kRowThreads + threadIdx.x) * 4;
+    v[j] = i < f ? *reinterpret_cast<const v4f *>(src + i) : v4f{0.f, 0.f, 0.f, 0.f};
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float r = 1.0f, s = 1.0f;
+  if (amax != 0.0f) {
+    r = kE4m3Max / amax;
+    s = amax / kE4m3Max;
+  }
+  uint8_t *dst = hq + (size_t)row * f;
+#pragma unroll
+  for (int j = 0; j < kRowVec; ++j) {
+    const int i = (j * kRowThreads + threadIdx.x) * 4;
+    if (i < f) *reinterpret_cast<uint32_t *>(dst + i) = e4m3x4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r);
+  }
+  if (threadIdx.x == 0) sh[row] = s;
+}
+
 // ------------------------------------------------------------------ combine
 // out[t] = sum_j w[t,j] * y[inv[t,j]] over valid slots in order, then + the
-// shared experts' rows in order.  One workgroup per token, 4 columns a lane.
+// shared experts' rows in order; each y row is the sum of its K-split slabs
+// in split order.  One workgroup per token, 4 columns a lane.
 __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *__restrict__ y,
-                                                      const int32_t *__restrict__ ids,
+                                                      int splits, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv,
                                                       float *__restrict__ out) {
   const int t = blockIdx.x;
   const int d = rs.d, K = rs.k_max;
+  const size_t slab = (size_t)(rs.capacity + rs.S * rs.T) * d;
+  auto yrow = [&](size_t row, int c) {
+    v4f v = *reinterpret_cast<const v4f *>(y + row * d + c);
+    for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const v4f *>(y + s * slab + row * d + c);
+    return v;
+  };
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < K; ++j) {
       const int p = t * K + j;
       if (ids[p] < 0) continue;
-      const float wj = w[p];
-      const v4f v = *reinterpret_cast<const v4f *>(y + (size_t)inv[p] * d + c);
-      acc += wj * v;
+      acc += w[p] * yrow((size_t)inv[p], c);
     }
-    for (int s = 0; s < rs.S; ++s) {
-      const v4f v =
-          *reinterpret_cast<const v4f *>(y + ((size_t)rs.capacity + (size_t)s * rs.T + t) * d + c);
-      acc += v;
-    }
+    for (int s = 0; s < rs.S; ++s) acc += yrow((size_t)rs.capacity + (size_t)s * rs.T + t, c);
     *reinterpret_cast<v4f *>(out + (size_t)t * d + c) = acc;
   }
 }
@@ -319,53 +445,70 @@ __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *
 
 static int grid_items(const RowSpace &rs) { return rs.items ? rs.max_items : rs.E + rs.S; }
 
+template <int MSUB, int NB, bool GATEUP>
+static hipError_t launch_ws(const GemmArgs &g, int n_tiles, hipStream_t stream) {
+  const int blocks = grid_items(g.rs) * n_tiles * g.splits;
+  if (blocks == 0) return hipSuccess;
+  wsgemm_kernel<MSUB, NB, GATEUP><<<blocks, 320, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+int32_t chunk_bytes(int32_t msub) { return 32768 / (16 * msub); }
+
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, hipStream_t stream) {
-  GemmArgs g{rs, xq, sx, nullptr, w, h};
-  const int blocks = grid_items(rs) * (rs.f >> 6);
-  if (blocks == 0) return hipSuccess;
-  if (msub >= 8)
-    gate_up_kernel<8><<<blocks, 256, 0, stream>>>(g);
-  else if (msub >= 4)
-    gate_up_kernel<4><<<blocks, 256, 0, stream>>>(g);
-  else if (msub >= 2)
-    gate_up_kernel<2><<<blocks, 256, 0, stream>>>(g);
-  else
-    gate_up_kernel<1><<<blocks, 256, 0, stream>>>(g);
-  return hipGetLastError();
+  GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
+  const int n_tiles = rs.f / 64;
+  if (msub >= 8) return launch_ws<8, 2, true>(g, n_tiles, stream);
+  if (msub >= 4) return launch_ws<4, 2, true>(g, n_tiles, stream);
+  if (msub >= 2) return launch_ws<2, 2, true>(g, n_tiles, stream);
+  return launch_ws<1, 2, true>(g, n_tiles, stream);
 }
 
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream) {
   const int rows_total = rs.capacity + rs.S * rs.T;
   if (rows_total == 0) return hipSuccess;
-  requant_kernel<<<(rows_total + 3) / 4, 256, 0, stream>>>(rs, h, hq, sh, rows_total);
+  requant_kernel<<<rows_total, kRowThreads, 0, stream>>>(rs, h, hq, sh);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
-                       const ExpertWeights &w, float *y, int32_t msub, hipStream_t stream) {
-  GemmArgs g{rs, hq, sh, h32, w, y};
-  const int blocks = grid_items(rs) * ((rs.d + 127) >> 7);
-  if (blocks == 0) return hipSuccess;
+                       const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
+                       hipStream_t stream) {
   if (h32) {
-    down_kernel<1, true><<<blocks, 256, 0, stream>>>(g);
-  } else if (msub >= 8) {
-    down_kernel<8, false><<<blocks, 256, 0, stream>>>(g);
-  } else if (msub >= 4) {
-    down_kernel<4, false><<<blocks, 256, 0, stream>>>(g);
-  } else if (msub >= 2) {
-    down_kernel<2, false><<<blocks, 256, 0, stream>>>(g);
-  } else {
-    down_kernel<1, false><<<blocks, 256, 0, stream>>>(g);
+    GemmArgs g{rs, nullptr, nullptr, h32, w, y, 1, rs.f};
+    const int blocks = grid_items(rs) * ((rs.d + 63) >> 6);
+    if (blocks == 0) return hipSuccess;
+    down_f32_kernel<<<blocks, 256, 0, stream>>>(g);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  const int kc = chunk_bytes(msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
+  const int nchunks = (rs.f + kc - 1) / kc;
+  splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
+  const int ksplit = ((nchunks + splits - 1) / splits) * kc;
+  splits = (rs.f + ksplit - 1) / ksplit;
+  GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
+  const int n_tiles = (rs.d + 63) / 64;
+  if (msub >= 8) return launch_ws<8, 1, false>(g, n_tiles, stream);
+  if (msub >= 4) return launch_ws<4, 1, false>(g, n_tiles, stream);
+  if (msub >= 2) return launch_ws<2, 1, false>(g, n_tiles, stream);
+  return launch_ws<1, 1, false>(g, n_tiles, stream);
 }
 
-hipError_t launch_combine(const RowSpace &rs, const float *y, const int32_t *ids, const float *w,
-                          const int32_t *inv_pairs, float *out, hipStream_t stream) {
+int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
+  const int kc = chunk_bytes(msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
+  const int nchunks = (f + kc - 1) / kc;
+  splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
+  const int ksplit = ((nchunks + splits - 1) / splits) * kc;
+  return (f + ksplit - 1) / ksplit;
+}
+
+hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
+                          const float *w, const int32_t *inv_pairs, float *out,
+                          hipStream_t stream) {
   if (rs.T == 0) return hipSuccess;
-  combine_kernel<<<rs.T, 256, 0, stream>>>(rs, y, ids, w, inv_pairs, out);
+  combine_kernel<<<rs.T, 256, 0, stream>>>(rs, y, splits, ids, w, inv_pairs, out);
   return hipGetLastError();
 }
 

@@ -75,11 +75,12 @@ enum {
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_K 32
 #define MOE_MAX_HIDDEN 16384 /* d: the router keeps a token's row in 64 KB of LDS */
+#define MOE_MAX_FFN 16384    /* f: requantisation keeps an h row in registers */
 
 typedef struct {
   int32_t T;        /* tokens, >= 1 */
   int32_t d;        /* hidden size, multiple of 64, at most MOE_MAX_HIDDEN */
-  int32_t f;        /* expert intermediate size, multiple of 64 */
+  int32_t f;        /* expert intermediate size, multiple of 64, at most MOE_MAX_FFN */
   int32_t E;        /* routed experts, 1..512 */
   int32_t k_max;    /* slots per token, 1..min(E, 32) */
   int32_t n_shared; /* always-on shared experts, >= 0 */
