@@ -68,8 +68,8 @@ _last_error = _sig("moe_last_error", C.c_char_p)
 _abi_version = _sig("moe_abi_version", _i32)
 _debug_stage_events = _sig("moe_debug_stage_events", _i32, C.POINTER(_vp), _i32)
 
-N_STAGE_EVENTS = 9
-STAGES = ("quantize", "router", "topk", "permute", "gate_up", "requant", "down", "combine")
+N_STAGE_EVENTS = 8
+STAGES = ("route", "topk", "permute", "gate_up", "requant", "down", "combine")
 
 ABI_VERSION = int(_abi_version())
 

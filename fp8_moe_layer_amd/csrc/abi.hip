@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/fp8moe.h"
@@ -94,7 +95,15 @@ int64_t capacity_of(int32_t T, int32_t E, int32_t k, int32_t bm) {
 // decode-sized batch keeps all of an expert's rows in one pass (its weights
 // then stream from HBM once).  mean + 4 sigma of a binomial expert load, in
 // units of 16 rows, rounded up to a power of two, at most 8.
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
 int32_t choose_msub(const moe_dims *d) {
+  // tile-tuning override (power of two, 1..8)
+  const int forced = env_int("FP8MOE_MSUB", 0);
+  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
   const double mean = (double)d->T * d->k_max / d->E;
   const double est = mean + 4.0 * sqrt(mean) + 2.0;
   int32_t m = 1;
@@ -106,6 +115,8 @@ int32_t choose_msub(const moe_dims *d) {
 // streaming when few experts are active (decode), one split otherwise.
 int32_t choose_down_splits(const moe_dims *d, int32_t msub) {
   if (d->flags & MOE_F_NO_REQUANT) return 1;
+  const int forced = env_int("FP8MOE_DOWN_SPLITS", 0);  // tile-tuning override
+  if (forced > 0) return down_splits_used(d->f, msub, forced);
   const double E = d->E;
   const double active = E * (1.0 - pow(1.0 - (double)d->k_max / E, (double)d->T)) + d->n_shared;
   const double tiles = (d->d + 63) / 64;
@@ -386,19 +397,20 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   };
 
   mark(0);
-  if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) return s;
-  mark(1);
   const float *lg = logits_override;
   if (!lg) {
-    if ((s = hip_status(launch_router(x, w_router, router_bias, dims->T, dims->d, dims->E, logits, st),
+    if ((s = hip_status(launch_route_logits(x, w_router, router_bias, dims->T, dims->d, dims->E,
+                                            logits, xq, sx, st),
                         "router")))
       return s;
     lg = logits;
+  } else if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) {
+    return s;
   }
-  mark(2);
+  mark(1);
   if ((s = hip_status(launch_topk(lg, dims->T, dims->E, dims->k_max, k_per_token, ids, tw, st), "topk")))
     return s;
-  mark(3);
+  mark(2);
   if ((s = hip_status(launch_permute(ids, dims->T, dims->E, dims->k_max, dims->block_m, L.capacity,
                                      sorted, offsets, block_expert, inv, n_blocks, items, n_items,
                                      L.row_chunk, dims->n_shared, st),
@@ -409,21 +421,21 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   rs.n_items = n_items;
   rs.max_items = L.max_items;
   const ExpertWeights ew = to_internal(w);
-  mark(4);
+  mark(3);
   if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, st), "gate_up"))) return s;
-  mark(5);
+  mark(4);
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
-    mark(6);
+    mark(5);
     if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, st), "down")))
       return s;
   } else {
-    mark(6);
+    mark(5);
     if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, st), "down"))) return s;
   }
-  mark(7);
+  mark(6);
   if ((s = hip_status(launch_combine(rs, y, L.splits, ids, tw, inv, out, st), "combine"))) return s;
-  mark(8);
+  mark(7);
   return ok();
 }
 

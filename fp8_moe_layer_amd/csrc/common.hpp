@@ -104,6 +104,41 @@ __device__ __forceinline__ void quantize_row_wave(const float *__restrict__ x, i
   if (lane == 0) *scale = s;
 }
 
+// One workgroup of NT threads per row, the row held in registers between the
+// max and the conversion (cols <= NT * 4 * VEC, cols a multiple of 4).  The
+// same IEEE operations as quantize_row_wave; `red` is NT/64 floats of LDS.
+template <int NT, int VEC>
+__device__ __forceinline__ void quantize_row_block(const float *__restrict__ x, int cols,
+                                                   uint8_t *__restrict__ q, float *scale,
+                                                   float *red) {
+  v4f v[VEC];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int i = (j * NT + (int)threadIdx.x) * 4;
+    v[j] = i < cols ? *reinterpret_cast<const v4f *>(x + i) : v4f{0.f, 0.f, 0.f, 0.f};
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) amax = fmaxf(amax, red[w]);
+  float r = 1.0f, s = 1.0f;
+  if (amax != 0.0f) {
+    r = kE4m3Max / amax;
+    s = amax / kE4m3Max;
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int i = (j * NT + (int)threadIdx.x) * 4;
+    if (i < cols)
+      *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r);
+  }
+  if (threadIdx.x == 0) *scale = s;
+}
+
 // ---------------------------------------------------------------- memory
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 

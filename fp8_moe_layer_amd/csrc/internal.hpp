@@ -39,6 +39,12 @@ hipError_t launch_quantize_rows(const float *x, int32_t rows, int32_t cols, uint
                                 float *scale, hipStream_t stream);
 hipError_t launch_router(const float *x, const float *w_router, const float *bias, int32_t T,
                          int32_t d, int32_t E, float *logits, hipStream_t stream);
+// Router logits plus (xq != nullptr) the per-token quantisation of x, fused
+// into one launch for decode-sized T*E.
+constexpr int64_t kRouterDotMax = 1 << 16;
+hipError_t launch_route_logits(const float *x, const float *w_router, const float *bias, int32_t T,
+                               int32_t d, int32_t E, float *logits, uint8_t *xq, float *sx,
+                               hipStream_t stream);
 hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
                        const int32_t *k_per_token, int32_t *ids, float *w, hipStream_t stream);
 // items/n_items/row_chunk: optional work list for the expert stages (row_chunk

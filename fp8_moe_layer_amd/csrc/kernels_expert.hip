@@ -13,14 +13,17 @@
 // in one item and each active expert's weights cross HBM exactly once.
 //
 // Workgroup = 4 compute waves + 1 loader wave (320 lanes):
-//  - the loader wave gathers the item's activation rows (e4m3) into LDS with
-//    global_load_lds_dwordx4, 32 KB chunks of K, double buffered;
+//  - the loader wave gathers the item's activation rows (e4m3) into a ring of
+//    four 16 KB LDS chunks with global_load_lds_dwordx4, three chunks ahead
+//    of the compute waves (exact vmcnt waits, so only the chunk due next is
+//    waited for);
 //  - each compute wave streams its own weight rows (16 output channels; the
 //    gate and the up row of each for the gate/up GEMM) straight from HBM
 //    into registers through a PF-deep prefetch ring, reads the activation
 //    fragments from LDS and runs v_mfma_f32_16x16x128_f8f6f4;
-//  - one s_barrier per chunk hands buffers between them.  The barrier waits
-//    only on LDS counters, so the weight prefetches stay in flight across it.
+//  - one s_barrier per chunk hands buffers between them.  The compute side
+//    waits only on LDS counters, so its weight prefetches stay in flight
+//    across it.
 //
 // MFMA operand layout (same for A = activation rows and B = weight rows):
 // lane l holds row l%16 and, of each 128-byte K step, the bytes
@@ -97,21 +100,32 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_piece[64];
 
 template <int MSUB>
 struct Chunk {
-  static constexpr int MP = 16 * MSUB;        // rows per pass
-  static constexpr int KC = 32768 / MP;       // K bytes per LDS chunk
-  static constexpr int KSC = KC / 128;        // K steps per chunk
+  static constexpr int MP = 16 * MSUB;           // rows per pass
+  static constexpr int KSC = 8 / MSUB;           // K steps per chunk: 16 KB of activations
   static constexpr int BYTES = MSUB * KSC * 2048;
-  // weight prefetch depth in k steps (deeper for the single-subtile case,
-  // which has the fewest MFMAs per byte and the registers to spare)
-  static constexpr int PF = MSUB == 1 ? 4 : 2;
+  static constexpr int NBUF = 4;                 // LDS ring; the loader runs NBUF-1 chunks ahead
+  static constexpr int LPC = MSUB * KSC * 2;     // direct-to-LDS loads per chunk (always 16)
+  // weight prefetch depth in k steps (registers allow 4 when few row tiles)
+  static constexpr int PF = MSUB <= 2 ? 4 : 2;
 };
+
+// s_waitcnt vmcnt(n * 16): n chunks of loads may stay in flight.
+__device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
+  if (chunks_in_flight >= 2)
+    asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+  else if (chunks_in_flight == 1)
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // GATEUP: out = h[rows][f], NB must be 2 (gate row, up row of the same channel).
 // else:   out = y[split][rows][d], NB channel groups of 16 per wave.
 template <int MSUB, int NB, bool GATEUP>
 __global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
   using C = Chunk<MSUB>;
-  __shared__ __attribute__((aligned(1024))) uint8_t abuf[2][C::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[C::NBUF][C::BYTES];
+  static_assert(C::LPC == 16 && C::NBUF == 4, "loader_wait_barrier assumes 16 loads per chunk");
 
   const RowSpace &rs = g.rs;
   const int K = GATEUP ? rs.d : rs.f;
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
   // K steps are processed PF at a time; steps past nks multiply zero
   // activation pieces by a repeat of the last weight step.
   const int nks_pf = (nks + C::PF - 1) / C::PF * C::PF;
-  const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;
+  const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;  // LDS chunks of KSC steps
   const bool half_tail = (k_end - k_begin) & 127;       // last step holds 64 bytes
 
   const bool shared = expert >= rs.E;
@@ -162,29 +176,30 @@ __global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
         }
         abase[m] = b;
       }
-      auto load_chunk = [&](int c) {
-        uint8_t *dst = abuf[c & 1];
-        const int steps = min(C::KSC, nks_pf - c * C::KSC);
+      auto issue = [&](int c) {
+        uint8_t *dst = abuf[c % C::NBUF];
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) {
-          if (m < msub) {
-            for (int s = 0; s < steps; ++s) {
 #pragma unroll
-              for (int p = 0; p < 2; ++p) {
-                const int kb = k_begin + (c * C::KSC + s) * 128 + p * 64 + kg * 16;
-                const uint8_t *src = (abase[m] && kb < k_end) ? abase[m] + kb : g_zero_piece;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ((m * C::KSC + s) * 2 + p) * 1024),
-                                                 16, 0, 0);
-              }
+          for (int s = 0; s < C::KSC; ++s) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const int kb = k_begin + (c * C::KSC + s) * 128 + p * 64 + kg * 16;
+              const uint8_t *src = (abase[m] && kb < k_end) ? abase[m] + kb : g_zero_piece;
+              __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ((m * C::KSC + s) * 2 + p) * 1024),
+                                               16, 0, 0);
             }
           }
         }
       };
-      load_chunk(0);
-      barrier_after_loads();
+      const int pre = min(C::NBUF - 1, nchunks);
+      for (int c = 0; c < pre; ++c) issue(c);
+      loader_wait_barrier(pre - 1);  // chunk 0 landed
       for (int c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) load_chunk(c + 1);
-        barrier_after_loads();
+        // chunk c+NBUF-1 reuses the buffer of chunk c-1, consumed before the last barrier
+        if (c + C::NBUF - 1 < nchunks) issue(c + C::NBUF - 1);
+        const int newest = min(c + C::NBUF - 1, nchunks - 1);
+        loader_wait_barrier(newest - (c + 1));  // chunk c+1 landed
       }
     }
     return;
@@ -243,7 +258,7 @@ __global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
       for (int s = 0; s < C::PF; ++s) {
         const int ks = ks0 + s;
         const int c = ks / C::KSC;
-        const uint8_t *fa = lds_lane + (c & 1) * C::BYTES + (ks - c * C::KSC) * 2048;
+        const uint8_t *fa = lds_lane + (c % C::NBUF) * C::BYTES + (ks - c * C::KSC) * 2048;
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) {
           if (m < msub) {
@@ -255,9 +270,8 @@ __global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
           }
         }
         load_b(ring[s], ks + C::PF);
+        if ((ks + 1) % C::KSC == 0 || ks + 1 == nks_pf) barrier_lds();  // end of chunk c
       }
-      const int next = ks0 + C::PF;
-      if (next % C::KSC == 0 || next == nks_pf) barrier_lds();
     }
 
     // ---------------- epilogue
@@ -384,38 +398,14 @@ __global__ __launch_bounds__(kRowThreads) void requant_kernel(RowSpace rs, const
   const int row = blockIdx.x;
   if (!row_real(rs, row)) return;
   __shared__ float red[kRowThreads / kWave];
-  const int f = rs.f;
-  const float *src = h + (size_t)row * f;
-  v4f v[kRowVec];
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kRowVec; ++j) {
-    const int i = (j * kRowThreads + threadIdx.x) * 4;
-    v[j] = i < f ? *reinterpret_cast<const v4f *>(src + i) : v4f{0.f, 0.f, 0.f, 0.f};
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
-  }
-  amax = wave_max(amax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float r = 1.0f, s = 1.0f;
-  if (amax != 0.0f) {
-    r = kE4m3Max / amax;
-    s = amax / kE4m3Max;
-  }
-  uint8_t *dst = hq + (size_t)row * f;
-#pragma unroll
-  for (int j = 0; j < kRowVec; ++j) {
-    const int i = (j * kRowThreads + threadIdx.x) * 4;
-    if (i < f) *reinterpret_cast<uint32_t *>(dst + i) = e4m3x4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r);
-  }
-  if (threadIdx.x == 0) sh[row] = s;
+  quantize_row_block<kRowThreads, kRowVec>(h + (size_t)row * rs.f, rs.f, hq + (size_t)row * rs.f,
+                                           sh + row, red);
 }
 
 // ------------------------------------------------------------------ combine
 // out[t] = sum_j w[t,j] * y[inv[t,j]] over valid slots in order, then + the
 // shared experts' rows in order; each y row is the sum of its K-split slabs
-// in split order.  One workgroup per token, 4 columns a lane.
+// in split order.  A workgroup per (token, 1024 columns), 4 columns a lane.
 __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *__restrict__ y,
                                                       int splits, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ w,
@@ -424,21 +414,21 @@ __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *
   const int t = blockIdx.x;
   const int d = rs.d, K = rs.k_max;
   const size_t slab = (size_t)(rs.capacity + rs.S * rs.T) * d;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= d) return;
   auto yrow = [&](size_t row, int c) {
     v4f v = *reinterpret_cast<const v4f *>(y + row * d + c);
     for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const v4f *>(y + s * slab + row * d + c);
     return v;
   };
-  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < K; ++j) {
-      const int p = t * K + j;
-      if (ids[p] < 0) continue;
-      acc += w[p] * yrow((size_t)inv[p], c);
-    }
-    for (int s = 0; s < rs.S; ++s) acc += yrow((size_t)rs.capacity + (size_t)s * rs.T + t, c);
-    *reinterpret_cast<v4f *>(out + (size_t)t * d + c) = acc;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < K; ++j) {
+    const int p = t * K + j;
+    if (ids[p] < 0) continue;
+    acc += w[p] * yrow((size_t)inv[p], c);
   }
+  for (int s = 0; s < rs.S; ++s) acc += yrow((size_t)rs.capacity + (size_t)s * rs.T + t, c);
+  *reinterpret_cast<v4f *>(out + (size_t)t * d + c) = acc;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -453,7 +443,8 @@ static hipError_t launch_ws(const GemmArgs &g, int n_tiles, hipStream_t stream) 
   return hipGetLastError();
 }
 
-int32_t chunk_bytes(int32_t msub) { return 32768 / (16 * msub); }
+// K bytes per LDS chunk for a row-pass size (the K-split granularity).
+int32_t chunk_bytes(int32_t msub) { return 128 * (8 / msub); }
 
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, hipStream_t stream) {
@@ -508,7 +499,8 @@ hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, co
                           const float *w, const int32_t *inv_pairs, float *out,
                           hipStream_t stream) {
   if (rs.T == 0) return hipSuccess;
-  combine_kernel<<<rs.T, 256, 0, stream>>>(rs, y, splits, ids, w, inv_pairs, out);
+  combine_kernel<<<dim3(rs.T, (rs.d + 1023) / 1024), 256, 0, stream>>>(rs, y, splits, ids, w,
+                                                                      inv_pairs, out);
   return hipGetLastError();
 }
 

@@ -20,14 +20,95 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float *__restr
                     threadIdx.x & 63);
 }
 
+// Rows up to 16384 values: a workgroup per row, the row in registers.
+__global__ __launch_bounds__(256) void quantize_rows_block_kernel(const float *__restrict__ x,
+                                                                  int cols, uint8_t *__restrict__ q,
+                                                                  float *__restrict__ scale) {
+  __shared__ float red[4];
+  const size_t row = blockIdx.x;
+  quantize_row_block<256, 16>(x + row * cols, cols, q + row * cols, scale + row, red);
+}
+
 hipError_t launch_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t *q,
                                 float *scale, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  quantize_rows_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(x, rows, cols, q, scale);
+  if (cols <= 16384)
+    quantize_rows_block_kernel<<<rows, 256, 0, stream>>>(x, cols, q, scale);
+  else
+    quantize_rows_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(x, rows, cols, q, scale);
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ router
+// ------------------------------------------------------------------ router, decode-sized
+// One wave per (token, expert) dot product over d, lanes striding d by 4
+// floats with all of a lane's loads issued before the FMAs.  The wave of
+// expert 0 also quantises its token's row (it has read the row already).
+constexpr int kDotVec = 8;  // float4 per lane per round: d <= 2048 in one round
+
+__global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict__ x,
+                                                         const float *__restrict__ wr,
+                                                         const float *__restrict__ bias, int T,
+                                                         int d, int E, float *__restrict__ logits,
+                                                         uint8_t *__restrict__ xq,
+                                                         float *__restrict__ sx) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= T * E) return;
+  const int lane = threadIdx.x & 63;
+  const int t = wid / E, e = wid - t * E;
+  const float *xr = x + (size_t)t * d;
+  const float *w = wr + (size_t)e * d;
+  float acc = 0.0f, amax = 0.0f;
+  for (int base = 0; base < d; base += kDotVec * 256) {
+    v4f xv[kDotVec], wv[kDotVec];
+#pragma unroll
+    for (int j = 0; j < kDotVec; ++j) {
+      const int i = base + (j * 64 + lane) * 4;
+      xv[j] = i < d ? *reinterpret_cast<const v4f *>(xr + i) : v4f{0.f, 0.f, 0.f, 0.f};
+      wv[j] = i < d ? *reinterpret_cast<const v4f *>(w + i) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kDotVec; ++j) {
+      acc = fmaf(xv[j].x, wv[j].x, acc);
+      acc = fmaf(xv[j].y, wv[j].y, acc);
+      acc = fmaf(xv[j].z, wv[j].z, acc);
+      acc = fmaf(xv[j].w, wv[j].w, acc);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv[j].x), fabsf(xv[j].y)),
+                               fmaxf(fabsf(xv[j].z), fabsf(xv[j].w))));
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
+  if (e == 0 && xq) {
+    amax = wave_max(amax);
+    float r = 1.0f, s = 1.0f;
+    if (amax != 0.0f) {
+      r = kE4m3Max / amax;
+      s = amax / kE4m3Max;
+    }
+    uint8_t *q = xq + (size_t)t * d;
+    for (int i = lane * 4; i < d; i += kWave * 4) {
+      const v4f v = *reinterpret_cast<const v4f *>(xr + i);
+      *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x * r, v.y * r, v.z * r, v.w * r);
+    }
+    if (lane == 0) sx[t] = s;
+  }
+}
+
+hipError_t launch_route_logits(const float *x, const float *w_router, const float *bias, int32_t T,
+                               int32_t d, int32_t E, float *logits, uint8_t *xq, float *sx,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if ((int64_t)T * E <= kRouterDotMax) {
+    router_dot_kernel<<<(T * E + 3) / 4, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits, xq,
+                                                           sx);
+    return hipGetLastError();
+  }
+  hipError_t e = hipSuccess;
+  if (xq && (e = launch_quantize_rows(x, T, d, xq, sx, stream)) != hipSuccess) return e;
+  return launch_router(x, w_router, bias, T, d, E, logits, stream);
+}
+
+// ------------------------------------------------------------------ router, tiled
 // logits[t][e] = x[t] . w_router[e] (+ bias[e]) in fp32.  A workgroup takes
 // TT tokens (kept in LDS) and a block of experts; each wave owns experts
 // e = block + wave, +4, ... and reduces TT dot products over d.
@@ -81,6 +162,11 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
 hipError_t launch_router(const float *x, const float *w_router, const float *bias, int32_t T,
                          int32_t d, int32_t E, float *logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if ((int64_t)T * E <= kRouterDotMax) {
+    router_dot_kernel<<<(T * E + 3) / 4, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits,
+                                                           nullptr, nullptr);
+    return hipGetLastError();
+  }
   // keep the token tile at <= 64 KB of LDS
   int tt = 16384 / d;
   int eb = E <= 64 ? E : 64;

@@ -207,13 +207,13 @@ moe_status moe_fused_forward(const moe_dims *dims /*host*/, const float *x, cons
 
 /* Stage timing (instrumentation, not part of the layer).  After this call,
  * moe_fused_forward on the calling thread records events[i] on its stream
- * just before stage i (0 quantise, 1 router, 2 top-k, 3 permutation,
- * 4 gate/up, 5 requantisation, 6 down, 7 combine) and events[8] after the
+ * just before stage i (0 quantise + router logits, 1 top-k, 2 permutation,
+ * 3 gate/up, 4 requantisation, 5 down, 6 combine) and events[7] after the
  * last one.  `events` is a host array of MOE_N_STAGE_EVENTS hipEvent_t
  * handles created and owned by the caller; the library keeps the pointer
  * until the next call.  Pass NULL, 0 to stop.  Returns MOE_ERR_SHAPE when
  * 0 < n_events < MOE_N_STAGE_EVENTS. */
-#define MOE_N_STAGE_EVENTS 9
+#define MOE_N_STAGE_EVENTS 8
 moe_status moe_debug_stage_events(void *const *events /*host*/, int32_t n_events);
 
 const char *moe_status_str(moe_status s);
