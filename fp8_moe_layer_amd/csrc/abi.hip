@@ -119,7 +119,7 @@ int32_t choose_down_splits(const moe_dims *d, int32_t msub) {
   if (forced > 0) return down_splits_used(d->f, msub, forced);
   const double E = d->E;
   const double active = E * (1.0 - pow(1.0 - (double)d->k_max / E, (double)d->T)) + d->n_shared;
-  const double tiles = (d->d + 63) / 64;
+  const double tiles = (d->d + kDownChannels - 1) / kDownChannels;
   int32_t s = (int32_t)ceil(1024.0 / (active * tiles));
   if (s < 1) s = 1;
   if (s > 8) s = 8;

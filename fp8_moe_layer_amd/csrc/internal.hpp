@@ -70,6 +70,7 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
                        hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
+constexpr int kDownChannels = 128;  // output channels per down-projection workgroup
 // out from y slabs summed in split order.
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
                           const float *w, const int32_t *inv_pairs, float *out,

@@ -480,11 +480,13 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   const int ksplit = ((nchunks + splits - 1) / splits) * kc;
   splits = (rs.f + ksplit - 1) / ksplit;
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
-  const int n_tiles = (rs.d + 63) / 64;
-  if (msub >= 8) return launch_ws<8, 1, false>(g, n_tiles, stream);
-  if (msub >= 4) return launch_ws<4, 1, false>(g, n_tiles, stream);
-  if (msub >= 2) return launch_ws<2, 1, false>(g, n_tiles, stream);
-  return launch_ws<1, 1, false>(g, n_tiles, stream);
+  // 32 channels per wave, 128 per workgroup: the activation rows each
+  // workgroup loads are shared by twice the weight bytes.
+  const int n_tiles = (rs.d + kDownChannels - 1) / kDownChannels;
+  if (msub >= 8) return launch_ws<8, 2, false>(g, n_tiles, stream);
+  if (msub >= 4) return launch_ws<4, 2, false>(g, n_tiles, stream);
+  if (msub >= 2) return launch_ws<2, 2, false>(g, n_tiles, stream);
+  return launch_ws<1, 2, false>(g, n_tiles, stream);
 }
 
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {

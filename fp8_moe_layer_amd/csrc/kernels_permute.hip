@@ -22,6 +22,7 @@ namespace fp8moe {
 
 constexpr int kPermWaves = 16;
 constexpr int kPermThreads = kPermWaves * kWave;
+constexpr int kBatch = 8;  // walk steps whose ids are loaded together
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -67,13 +68,23 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int b0 = min(P, wave * per), b1 = min(P, b0 + per);
   int *my = cnt + wave * E;
 
-  // pass 1: per-wave counts
-  for (int base = b0; base < b1; base += kWave) {
-    const int p = base + lane;
-    const int e = p < b1 ? ids[p] : -1;
-    const bool valid = e >= 0;
-    const uint64_t m = same_expert_mask(e, valid, nbits);
-    if (valid && __popcll(m & lt_mask) == 0) my[e] += __popcll(m);
+  // pass 1: per-wave counts (the slice's ids are fetched kBatch steps at a
+  // time so the loads overlap instead of serialising the walk)
+  for (int base = b0; base < b1; base += kWave * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = base + u * kWave + lane;
+      ev[u] = p < b1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = ev[u];
+      const bool valid = e >= 0;
+      const uint64_t m = same_expert_mask(e, valid, nbits);
+      if (valid && __popcll(m & lt_mask) == 0) my[e] += __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   __syncthreads();
 
@@ -143,23 +154,32 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 
   // pass 2: scatter (rows from base + running count + rank in the step)
-  for (int base = b0; base < b1; base += kWave) {
-    const int p = base + lane;
-    const int e = p < b1 ? ids[p] : -1;
-    const bool valid = e >= 0;
-    const uint64_t m = same_expert_mask(e, valid, nbits);
-    if (valid) {
-      const int rank = __popcll(m & lt_mask);
-      const int row = off[e] + my[e] + rank;
-      sorted_pairs[row] = p;
-      inv_pairs[p] = row;
-      // the leader's update is ordered after every lane's read above (same wave)
-      __builtin_amdgcn_wave_barrier();
-      if (rank == 0) my[e] += __popcll(m);
-    } else if (p < b1) {
-      inv_pairs[p] = -1;
+  for (int base = b0; base < b1; base += kWave * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = base + u * kWave + lane;
+      ev[u] = p < b1 ? ids[p] : -1;
     }
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = base + u * kWave + lane;
+      const int e = ev[u];
+      const bool valid = e >= 0;
+      const uint64_t m = same_expert_mask(e, valid, nbits);
+      if (valid) {
+        const int rank = __popcll(m & lt_mask);
+        const int row = off[e] + my[e] + rank;
+        sorted_pairs[row] = p;
+        inv_pairs[p] = row;
+        // the leader's update is ordered after every lane's read above (same wave)
+        __builtin_amdgcn_wave_barrier();
+        if (rank == 0) my[e] += __popcll(m);
+      } else if (p < b1) {
+        inv_pairs[p] = -1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 

@@ -109,52 +109,76 @@ hipError_t launch_route_logits(const float *x, const float *w_router, const floa
 }
 
 // ------------------------------------------------------------------ router, tiled
-// logits[t][e] = x[t] . w_router[e] (+ bias[e]) in fp32.  A workgroup takes
-// TT tokens (kept in LDS) and a block of experts; each wave owns experts
-// e = block + wave, +4, ... and reduces TT dot products over d.
-template <int TT>
-__global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x,
-                                                     const float *__restrict__ wr,
-                                                     const float *__restrict__ bias, int T, int d,
-                                                     int E, int eb, float *__restrict__ logits) {
-  extern __shared__ float xs[];  // [TT][d]
-  const int t0 = blockIdx.x * TT;
-  const int nt = min(TT, T - t0);
-  for (int i = threadIdx.x * 4; i < TT * d; i += 256 * 4) {
-    int tt = i / d;
-    v4f v = {0.f, 0.f, 0.f, 0.f};
-    if (tt < nt) v = *reinterpret_cast<const v4f *>(x + (size_t)t0 * d + i);
-    *reinterpret_cast<v4f *>(xs + i) = v;
+// Batches with many (token, expert) pairs: logits = X . W_r^T as an fp32
+// GEMM on v_mfma_f32_16x16x4_f32.  A workgroup computes 32 tokens x 64
+// experts; K advances 64 floats at a time through LDS (rows padded to 68
+// floats so the per-lane reads hit distinct banks), the next chunk's global
+// loads in flight while the current one is multiplied.  Wave w owns tokens
+// [16*(w&1), +16) x experts [32*(w>>1), +32): two 16x16 tiles.
+constexpr int kRT = 32, kRE = 64, kRK = 64, kRS = kRK + 4;
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const float *__restrict__ x,
+                                                          const float *__restrict__ wr,
+                                                          const float *__restrict__ bias, int T,
+                                                          int d, int E, float *__restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) float xs[kRT * kRS];
+  __shared__ __attribute__((aligned(16))) float ws[kRE * kRS];
+  const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int th = wave & 1, eh = wave >> 1;
+  const int lr = lane & 15, lk = lane >> 4;
+  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // the next K chunk is fetched into registers while the current one is used
+  constexpr int XJ = kRT * kRK / 4 / 256, WJ = kRE * kRK / 4 / 256;
+  v4f xr[XJ], wrg[WJ];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int i = tid + j * 256, r = i >> 4, c = (i & 15) * 4;
+      xr[j] = t0 + r < T ? *reinterpret_cast<const v4f *>(x + (size_t)(t0 + r) * d + k0 + c)
+                         : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int i = tid + j * 256, r = i >> 4, c = (i & 15) * 4;
+      wrg[j] = e0 + r < E ? *reinterpret_cast<const v4f *>(wr + (size_t)(e0 + r) * d + k0 + c)
+                          : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < d; k0 += kRK) {
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int i = tid + j * 256;
+      *reinterpret_cast<v4f *>(xs + (i >> 4) * kRS + (i & 15) * 4) = xr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int i = tid + j * 256;
+      *reinterpret_cast<v4f *>(ws + (i >> 4) * kRS + (i & 15) * 4) = wrg[j];
+    }
+    __syncthreads();
+    if (k0 + kRK < d) fetch(k0 + kRK);
+    const float *xa = xs + (16 * th + lr) * kRS + lk;
+    const float *wb0 = ws + (32 * eh + lr) * kRS + lk;
+    const float *wb1 = wb0 + 16 * kRS;
+#pragma unroll
+    for (int kk = 0; kk < kRK; kk += 4) {
+      const float a = xa[kk];
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, wb0[kk], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, wb1[kk], acc[1], 0, 0, 0);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e0 = blockIdx.y * eb;
-  const int e1 = min(E, e0 + eb);
-  for (int e = e0 + wave; e < e1; e += 4) {
-    float acc[TT];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
-    const float *w = wr + (size_t)e * d;
-    for (int i = lane * 4; i < d; i += kWave * 4) {
-      v4f wv = *reinterpret_cast<const v4f *>(w + i);
+  for (int n = 0; n < 2; ++n) {
+    const int e = e0 + 32 * eh + 16 * n + lr;
+    if (e >= E) continue;
+    const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        v4f xv = *reinterpret_cast<const v4f *>(xs + t * d + i);
-        acc[t] = fmaf(wv.x, xv.x, acc[t]);
-        acc[t] = fmaf(wv.y, xv.y, acc[t]);
-        acc[t] = fmaf(wv.z, xv.z, acc[t]);
-        acc[t] = fmaf(wv.w, xv.w, acc[t]);
-      }
-    }
-    float mine = 0.0f;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      float s = wave_sum(acc[t]);
-      if (lane == t) mine = s;
-    }
-    if (lane < nt) {
-      if (bias) mine += bias[e];
-      logits[(size_t)(t0 + lane) * E + e] = mine;
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * th + 4 * lk + i;
+      if (t < T) logits[(size_t)t * E + e] = bias ? acc[n][i] + b : acc[n][i];
     }
   }
 }
@@ -167,27 +191,8 @@ hipError_t launch_router(const float *x, const float *w_router, const float *bia
                                                            nullptr, nullptr);
     return hipGetLastError();
   }
-  // keep the token tile at <= 64 KB of LDS
-  int tt = 16384 / d;
-  int eb = E <= 64 ? E : 64;
-  dim3 block(256);
-  if (tt >= 16) {
-    dim3 grid((T + 15) / 16, (E + eb - 1) / eb);
-    router_kernel<16><<<grid, block, 16 * d * sizeof(float), stream>>>(x, w_router, bias, T, d, E,
-                                                                        eb, logits);
-  } else if (tt >= 8) {
-    dim3 grid((T + 7) / 8, (E + eb - 1) / eb);
-    router_kernel<8><<<grid, block, 8 * d * sizeof(float), stream>>>(x, w_router, bias, T, d, E, eb,
-                                                                      logits);
-  } else if (tt >= 4) {
-    dim3 grid((T + 3) / 4, (E + eb - 1) / eb);
-    router_kernel<4><<<grid, block, 4 * d * sizeof(float), stream>>>(x, w_router, bias, T, d, E, eb,
-                                                                      logits);
-  } else {
-    dim3 grid(T, (E + eb - 1) / eb);
-    router_kernel<1><<<grid, block, d * sizeof(float), stream>>>(x, w_router, bias, T, d, E, eb,
-                                                                  logits);
-  }
+  dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
+  router_mfma_kernel<<<grid, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits);
   return hipGetLastError();
 }
 

@@ -65,7 +65,10 @@ def test_quantize_rows_bit_exact(rows, cols):
 
 @pytest.mark.parametrize("T,d,E,bias", [(1, 4096, 8, False), (37, 2048, 128, True),
                                         (100, 256, 8, False), (16, 2048, 512, True),
-                                        (5, 64, 3, True)])
+                                        (5, 64, 3, True),
+                                        # batches past the per-(token, expert) kernel: tiled fp32 MFMA path
+                                        (1000, 320, 100, True), (4096, 2048, 128, False),
+                                        (1024, 2048, 512, True)])
 def test_router_logits(T, d, E, bias):
     g = torch.Generator().manual_seed(T + d + E)
     x = torch.randn(T, d, generator=g)
@@ -77,16 +80,17 @@ def test_router_logits(T, d, E, bias):
     assert err < 1e-5, err
 
 
-def test_router_one_hot_exact():
-    d, E = 256, 16
+@pytest.mark.parametrize("T,E", [(3, 16), (3000, 40)])
+def test_router_one_hot_exact(T, E):
+    d = 256
     g = torch.Generator().manual_seed(3)
     wr = torch.randn(E, d, generator=g)
     b = torch.randn(E, generator=g)
-    x = torch.zeros(3, d)
-    x[0, 0] = x[1, 100] = x[2, 255] = 1.0
+    cols = torch.randint(0, d, (T,), generator=g)
+    x = torch.zeros(T, d)
+    x[torch.arange(T), cols] = 1.0
     lg = to_np(lib().router_logits(x.to(dev()), wr.to(dev()), b.to(dev())))
-    for r, i in enumerate([0, 100, 255]):
-        np.testing.assert_array_equal(lg[r], (wr[:, i] + b).numpy())
+    np.testing.assert_array_equal(lg, (wr[:, cols].T + b).numpy())
 
 
 # ----------------------------------------------------------------- top-k
