@@ -19,6 +19,7 @@ _HERE = pathlib.Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libfp8moe.so"
 
 MOE_F_NO_REQUANT = 1
+MOE_F_PERSISTENT = 2
 MAX_EXPERTS = 512
 MAX_K = 32
 
@@ -222,8 +223,9 @@ class DeviceWeights:
 
 # --------------------------------------------------------------------------- expert stages
 
-def dims(T, d, f, E, k_max, n_shared=0, block_m=16, no_requant=False) -> Dims:
-    return Dims(T, d, f, E, k_max, n_shared, block_m, MOE_F_NO_REQUANT if no_requant else 0)
+def dims(T, d, f, E, k_max, n_shared=0, block_m=16, no_requant=False, persistent=False) -> Dims:
+    flags = (MOE_F_NO_REQUANT if no_requant else 0) | (MOE_F_PERSISTENT if persistent else 0)
+    return Dims(T, d, f, E, k_max, n_shared, block_m, flags)
 
 
 def expert_gate_up(dm: Dims, perm: dict, xq, sx, w: DeviceWeights, stream=None):
@@ -265,25 +267,27 @@ class MoELayer:
 
     forward(x) runs the whole layer (quantise, router, top-k, permutation,
     gate/up + SiLU*up, requantisation, down projection, combine) in the
-    library's kernels on the current stream.  The workspace is allocated once
+    library's kernels on the current stream -- seven launches, or one
+    cooperative launch with persistent=True.  The workspace is allocated once
     per token count and reused.
     """
 
     def __init__(self, weights: DeviceWeights, w_router: Optional[torch.Tensor], k_max: int,
                  router_bias: Optional[torch.Tensor] = None, block_m: int = 16,
-                 no_requant: bool = False):
+                 no_requant: bool = False, persistent: bool = False):
         self.w = weights
         self.w_router = w_router
         self.router_bias = router_bias
         self.k_max = k_max
         self.block_m = block_m
         self.no_requant = no_requant
+        self.persistent = persistent
         self._ws = {}
         self._wstruct = weights.struct()
 
     def dims(self, T: int) -> Dims:
         return dims(T, self.w.d, self.w.f, self.w.E, self.k_max, self.w.n_shared, self.block_m,
-                    self.no_requant)
+                    self.no_requant, self.persistent)
 
     def workspace(self, T: int, device) -> torch.Tensor:
         ws = self._ws.get(T)

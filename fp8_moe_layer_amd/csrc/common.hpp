@@ -17,6 +17,7 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 512;  // routed experts per layer (top-k keys, permutation LDS)
 constexpr int kMaxK = 32;         // slots per token
+constexpr int kMaxFfn = 16384;  // longest h row the requantisation holds in registers
 constexpr float kE4m3Max = 448.0f;
 
 // ---------------------------------------------------------------- e4m3 codec

@@ -70,10 +70,41 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
                        hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
+// K bytes per LDS chunk of the grouped GEMMs for a row-pass size.
+int32_t chunk_bytes(int32_t msub);
+// Final K-split count and bytes per split for a requested split count.
+void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
+                         int32_t *ksplit);
 constexpr int kDownChannels = 128;  // output channels per down-projection workgroup
 // out from y slabs summed in split order.
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
                           const float *w, const int32_t *inv_pairs, float *out,
                           hipStream_t stream);
+
+// Everything the single-launch (persistent) layer needs: the same buffers
+// as the per-stage path.
+struct PersistentLaunch {
+  RowSpace rs;  // with the work list
+  ExpertWeights w;
+  const float *x, *w_router, *bias;
+  const int32_t *kpt;
+  const float *logits_override;
+  float *logits;
+  uint8_t *xq;
+  float *sx;
+  int32_t *ids;
+  float *tw;
+  int32_t *sorted, *offsets, *block_expert, *inv, *n_blocks;
+  WorkItem *items;
+  int32_t *n_items;
+  float *h;
+  uint8_t *hq;
+  float *sh, *y, *out;
+  int32_t block_m, row_chunk, msub, splits;
+};
+// One cooperative launch; returns the launch error
+// (hipErrorCooperativeLaunchTooLarge when the grid cannot be resident).
+// Switched off: not called (see kernels_persistent.hip).
+hipError_t launch_persistent(const PersistentLaunch &p, hipStream_t stream);
 
 }  // namespace fp8moe

@@ -32,297 +32,15 @@
 // element i = C[4*(l/16) + i][l%16].
 #include "common.hpp"
 #include "internal.hpp"
+#include "expert_dev.hpp"
 
 namespace fp8moe {
 
-namespace {
-
-struct GemmArgs {
-  RowSpace rs;
-  const uint8_t *a;      // gate/up: xq [T][d]; down: hq [rows][f]
-  const float *a_scale;  // sx [T] or sh [rows]
-  const float *a32;      // down, fp32 mode: h [rows][f]
-  ExpertWeights w;
-  float *out;            // h [rows][f] or y [splits][rows][d]
-  int32_t splits;        // K splits (down only; partial sums go to separate y slabs)
-  int32_t ksplit;        // bytes of K per split (multiple of the chunk size)
-};
-
-__device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, int &expert,
-                                             int &row0, int &rows) {
-  if (rs.items) {
-    if (item_id >= *rs.n_items) return false;
-    const WorkItem it = rs.items[item_id];
-    expert = it.expert;
-    row0 = it.row0;
-    rows = it.rows;
-  } else {
-    expert = item_id;
-    if (expert < rs.E) {
-      row0 = rs.expert_offsets[expert];
-      rows = rs.expert_offsets[expert + 1] - row0;
-    } else {
-      row0 = rs.capacity + (expert - rs.E) * rs.T;
-      rows = rs.T;
-    }
-  }
-  return rows > 0;
-}
-
-// Token of an expert row, or -1 for a padding row.
-__device__ __forceinline__ int row_token(const RowSpace &rs, int grow) {
-  if (grow >= rs.capacity) return (grow - rs.capacity) % rs.T;
-  const int p = rs.sorted_pairs[grow];
-  return p >= rs.T * rs.k_max ? -1 : p / rs.k_max;
-}
-
-__device__ __forceinline__ bool row_real(const RowSpace &rs, int grow) {
-  return grow >= rs.capacity || rs.sorted_pairs[grow] < rs.T * rs.k_max;
-}
-
-// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
-// its outstanding global loads.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Loader side: its direct-to-LDS loads are counted by vmcnt.
-__device__ __forceinline__ void barrier_after_loads() {
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void *lds_ptr;
-
-}  // namespace
-
-// 64 zero bytes: the source of activation pieces for padding rows and K
-// past the end.  Never written.
-__device__ __attribute__((aligned(64))) uint8_t g_zero_piece[64];
-
 // ------------------------------------------------------------------ grouped GEMM
-
-template <int MSUB>
-struct Chunk {
-  static constexpr int MP = 16 * MSUB;           // rows per pass
-  static constexpr int KSC = 8 / MSUB;           // K steps per chunk: 16 KB of activations
-  static constexpr int BYTES = MSUB * KSC * 2048;
-  static constexpr int NBUF = 4;                 // LDS ring; the loader runs NBUF-1 chunks ahead
-  static constexpr int LPC = MSUB * KSC * 2;     // direct-to-LDS loads per chunk (always 16)
-  // weight prefetch depth in k steps (registers allow 4 when few row tiles)
-  static constexpr int PF = MSUB <= 2 ? 4 : 2;
-};
-
-// s_waitcnt vmcnt(n * 16): n chunks of loads may stay in flight.
-__device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
-  if (chunks_in_flight >= 2)
-    asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
-  else if (chunks_in_flight == 1)
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// GATEUP: out = h[rows][f], NB must be 2 (gate row, up row of the same channel).
-// else:   out = y[split][rows][d], NB channel groups of 16 per wave.
 template <int MSUB, int NB, bool GATEUP>
 __global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
-  using C = Chunk<MSUB>;
-  __shared__ __attribute__((aligned(1024))) uint8_t abuf[C::NBUF][C::BYTES];
-  static_assert(C::LPC == 16 && C::NBUF == 4, "loader_wait_barrier assumes 16 loads per chunk");
-
-  const RowSpace &rs = g.rs;
-  const int K = GATEUP ? rs.d : rs.f;
-  const int N = GATEUP ? rs.f : rs.d;
-  constexpr int CH_WAVE = GATEUP ? 16 : 16 * NB;
-  constexpr int CH_WG = 4 * CH_WAVE;
-  const int n_tiles = (N + CH_WG - 1) / CH_WG;
-  int bid = blockIdx.x;
-  const int split = bid % g.splits;
-  bid /= g.splits;
-  const int tile = bid % n_tiles;
-  const int item_id = bid / n_tiles;
-  int expert, row0, rows;
-  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
-  const int k_begin = split * g.ksplit;
-  const int k_end = min(K, k_begin + g.ksplit);
-  if (k_begin >= k_end) return;
-  const int nks = (k_end - k_begin + 127) >> 7;         // K steps in this split
-  // K steps are processed PF at a time; steps past nks multiply zero
-  // activation pieces by a repeat of the last weight step.
-  const int nks_pf = (nks + C::PF - 1) / C::PF * C::PF;
-  const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;  // LDS chunks of KSC steps
-  const bool half_tail = (k_end - k_begin) & 127;       // last step holds 64 bytes
-
-  const bool shared = expert >= rs.E;
-  const size_t ex = (size_t)(shared ? expert - rs.E : expert);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int ln = lane & 15, kg = lane >> 4;
-
-  if (wave == 4) {
-    // ---------------- loader wave: activation rows -> LDS, chunk by chunk
-    const uint8_t *abase[MSUB];
-    for (int p0 = 0; p0 < rows; p0 += C::MP) {
-      const int prow = min(C::MP, rows - p0);
-      const int msub = (prow + 15) >> 4;
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        const int r = p0 + m * 16 + ln;
-        const uint8_t *b = nullptr;
-        if (m < msub && r < rows) {
-          if (GATEUP) {
-            const int tok = row_token(rs, row0 + r);
-            if (tok >= 0) b = g.a + (size_t)tok * K;
-          } else if (row_real(rs, row0 + r)) {
-            b = g.a + (size_t)(row0 + r) * K;
-          }
-        }
-        abase[m] = b;
-      }
-      auto issue = [&](int c) {
-        uint8_t *dst = abuf[c % C::NBUF];
-#pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
-#pragma unroll
-          for (int s = 0; s < C::KSC; ++s) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              const int kb = k_begin + (c * C::KSC + s) * 128 + p * 64 + kg * 16;
-              const uint8_t *src = (abase[m] && kb < k_end) ? abase[m] + kb : g_zero_piece;
-              __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ((m * C::KSC + s) * 2 + p) * 1024),
-                                               16, 0, 0);
-            }
-          }
-        }
-      };
-      const int pre = min(C::NBUF - 1, nchunks);
-      for (int c = 0; c < pre; ++c) issue(c);
-      loader_wait_barrier(pre - 1);  // chunk 0 landed
-      for (int c = 0; c < nchunks; ++c) {
-        // chunk c+NBUF-1 reuses the buffer of chunk c-1, consumed before the last barrier
-        if (c + C::NBUF - 1 < nchunks) issue(c + C::NBUF - 1);
-        const int newest = min(c + C::NBUF - 1, nchunks - 1);
-        loader_wait_barrier(newest - (c + 1));  // chunk c+1 landed
-      }
-    }
-    return;
-  }
-
-  // ---------------- compute waves
-  const uint8_t *bw[NB];
-  int ch[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    int o;
-    const uint8_t *wbase;
-    if (GATEUP) {
-      o = tile * CH_WG + wave * 16 + ln;
-      wbase = (nb == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
-              ex * (size_t)N * K;
-    } else {
-      o = tile * CH_WG + wave * CH_WAVE + nb * 16 + ln;
-      wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * K;
-    }
-    ch[nb] = o;
-    const int orow = o < N ? o : N - 1;  // a partial last tile re-reads a valid row
-    bw[nb] = wbase + (size_t)orow * K + k_begin + kg * 16;
-  }
-  // Weight pieces of k step ks: +ks*128 and +ks*128+64.  Past the end the step
-  // is clamped to the last one; in a 64-byte tail step the second piece
-  // repeats the first (its activation piece is zero).
-  auto load_b = [&](v8i (&b)[NB], int ks) {
-    ks = min(ks, nks - 1);
-    const int o0 = ks * 128;
-    const int o1 = (half_tail && ks == nks - 1) ? o0 : o0 + 64;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const v4i lo = load16(bw[nb] + o0);
-      const v4i hi = load16(bw[nb] + o1);
-      b[nb] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-  };
-
-  v8i ring[C::PF][NB];
-  v4f acc[MSUB][NB];
-  const uint8_t *lds_lane = &abuf[0][0] + lane * 16;
-  for (int p0 = 0; p0 < rows; p0 += C::MP) {
-    const int prow = min(C::MP, rows - p0);
-    const int msub = (prow + 15) >> 4;
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[m][nb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < C::PF; ++s) load_b(ring[s], s);
-    barrier_lds();
-
-    for (int ks0 = 0; ks0 < nks_pf; ks0 += C::PF) {
-#pragma unroll
-      for (int s = 0; s < C::PF; ++s) {
-        const int ks = ks0 + s;
-        const int c = ks / C::KSC;
-        const uint8_t *fa = lds_lane + (c % C::NBUF) * C::BYTES + (ks - c * C::KSC) * 2048;
-#pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
-          if (m < msub) {
-            const v4i a0 = *reinterpret_cast<const v4i *>(fa + m * C::KSC * 2048);
-            const v4i a1 = *reinterpret_cast<const v4i *>(fa + m * C::KSC * 2048 + 1024);
-            const v8i a = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[m][nb] = mfma_e4m3_16x16x128(a, ring[s][nb], acc[m][nb]);
-          }
-        }
-        load_b(ring[s], ks + C::PF);
-        if ((ks + 1) % C::KSC == 0 || ks + 1 == nks_pf) barrier_lds();  // end of chunk c
-      }
-    }
-
-    // ---------------- epilogue
-    if (GATEUP) {
-      const int o = ch[0];
-      const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + o];
-      const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + o];
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        if (m < msub) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = p0 + m * 16 + kg * 4 + i;
-            if (r < rows) {
-              const int grow = row0 + r;
-              const int tok = row_token(rs, grow);
-              float hv = 0.0f;
-              if (tok >= 0) {
-                const float sxt = g.a_scale[tok];
-                const float gv = acc[m][0][i] * sxt * sgo;
-                const float uv = acc[m][1][i] * sxt * suo;
-                hv = gv / (1.0f + expf(-gv)) * uv;
-              }
-              g.out[(size_t)grow * N + o] = hv;
-            }
-          }
-        }
-      }
-    } else {
-      const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * N;
-      float *ys = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N;
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        if (m < msub) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = p0 + m * 16 + kg * 4 + i;
-            if (r < rows) {
-              const int grow = row0 + r;
-              const bool real = row_real(rs, grow);
-              const float shr = real ? g.a_scale[grow] : 0.0f;
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb) {
-                if (ch[nb] < N) ys[(size_t)grow * N + ch[nb]] = real ? acc[m][nb][i] * shr * sd[ch[nb]] : 0.0f;
-              }
-            }
-          }
-        }
-      }
-    }
-  }
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[kGemmLdsBytes];
+  wsgemm_tile<MSUB, NB, GATEUP>(g, blockIdx.x, abuf);
 }
 
 // ------------------------------------------------------------------ down, fp32 products
@@ -387,48 +105,22 @@ __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ requant
-// One workgroup per real expert row: hq = e4m3(h * 448/amax), sh = amax/448,
-// the row held in registers between the max and the conversion.
 constexpr int kRowThreads = 256;
-constexpr int kRowVec = 16;  // float4 per thread: rows up to 16384 values
 
 __global__ __launch_bounds__(kRowThreads) void requant_kernel(RowSpace rs, const float *__restrict__ h,
                                                               uint8_t *__restrict__ hq,
                                                               float *__restrict__ sh) {
-  const int row = blockIdx.x;
-  if (!row_real(rs, row)) return;
   __shared__ float red[kRowThreads / kWave];
-  quantize_row_block<kRowThreads, kRowVec>(h + (size_t)row * rs.f, rs.f, hq + (size_t)row * rs.f,
-                                           sh + row, red);
+  requant_row<kRowThreads>(rs, h, hq, sh, blockIdx.x, red);
 }
 
 // ------------------------------------------------------------------ combine
-// out[t] = sum_j w[t,j] * y[inv[t,j]] over valid slots in order, then + the
-// shared experts' rows in order; each y row is the sum of its K-split slabs
-// in split order.  A workgroup per (token, 1024 columns), 4 columns a lane.
 __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *__restrict__ y,
                                                       int splits, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv,
                                                       float *__restrict__ out) {
-  const int t = blockIdx.x;
-  const int d = rs.d, K = rs.k_max;
-  const size_t slab = (size_t)(rs.capacity + rs.S * rs.T) * d;
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (c >= d) return;
-  auto yrow = [&](size_t row, int c) {
-    v4f v = *reinterpret_cast<const v4f *>(y + row * d + c);
-    for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const v4f *>(y + s * slab + row * d + c);
-    return v;
-  };
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < K; ++j) {
-    const int p = t * K + j;
-    if (ids[p] < 0) continue;
-    acc += w[p] * yrow((size_t)inv[p], c);
-  }
-  for (int s = 0; s < rs.S; ++s) acc += yrow((size_t)rs.capacity + (size_t)s * rs.T + t, c);
-  *reinterpret_cast<v4f *>(out + (size_t)t * d + c) = acc;
+  combine_chunk<256>(rs, y, splits, ids, w, inv, out, blockIdx.x, blockIdx.y * 1024);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -464,6 +156,21 @@ hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float
   return hipGetLastError();
 }
 
+void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
+                         int32_t *ksplit) {
+  const int kc = chunk_bytes(msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
+  const int nchunks = (f + kc - 1) / kc;
+  const int s = requested < 1 ? 1 : (requested > nchunks ? nchunks : requested);
+  *ksplit = ((nchunks + s - 1) / s) * kc;
+  *splits = (f + *ksplit - 1) / *ksplit;
+}
+
+int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
+  int32_t s, k;
+  down_split_geometry(f, msub, splits, &s, &k);
+  return s;
+}
+
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
                        hipStream_t stream) {
@@ -474,11 +181,8 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
     down_f32_kernel<<<blocks, 256, 0, stream>>>(g);
     return hipGetLastError();
   }
-  const int kc = chunk_bytes(msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
-  const int nchunks = (rs.f + kc - 1) / kc;
-  splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
-  const int ksplit = ((nchunks + splits - 1) / splits) * kc;
-  splits = (rs.f + ksplit - 1) / ksplit;
+  int32_t ksplit;
+  down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
   // 32 channels per wave, 128 per workgroup: the activation rows each
   // workgroup loads are shared by twice the weight bytes.
@@ -487,14 +191,6 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   if (msub >= 4) return launch_ws<4, 2, false>(g, n_tiles, stream);
   if (msub >= 2) return launch_ws<2, 2, false>(g, n_tiles, stream);
   return launch_ws<1, 2, false>(g, n_tiles, stream);
-}
-
-int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
-  const int kc = chunk_bytes(msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
-  const int nchunks = (f + kc - 1) / kc;
-  splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
-  const int ksplit = ((nchunks + splits - 1) / splits) * kc;
-  return (f + ksplit - 1) / ksplit;
 }
 
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,

@@ -1,48 +1,13 @@
-// kernels_permute.hip -- deterministic expert-sorted permutation (dispatch on
-// one device) for gfx950.
-//
-// "Routage MoE entre GPU": each token's activation is moved to the experts
-// it selected, and at the end the weighted outputs are put back in the
-// original token order.  On one device that movement is a grouping of the
-// (token, slot) pairs by expert, padded to the GEMM row tile, plus the
-// inverse map used by the combine.
-//
-// One workgroup of 16 waves.  Each wave owns a contiguous slice of the pairs
-// and walks it 64 at a time; lanes holding the same expert find each other
-// with one ballot per expert-id bit, so a pair's rank among equal experts
-// before it in the slice comes from a popcount, never from an atomic ticket.
-// Pass 1 counts per (wave, expert); a prefix over waves and an exclusive scan
-// over the padded per-expert totals give every pair its row; pass 2 repeats
-// the walk and scatters.  The order inside a segment is therefore ascending
-// pair index, and the result is unique.
+// kernels_permute.hip -- the permutation (dispatch on one device) as one
+// 16-wave workgroup; the algorithm is in permute_dev.hpp.
 #include "common.hpp"
 #include "internal.hpp"
+#include "permute_dev.hpp"
 
 namespace fp8moe {
 
 constexpr int kPermWaves = 16;
 constexpr int kPermThreads = kPermWaves * kWave;
-constexpr int kBatch = 8;  // walk steps whose ids are loaded together
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
-// Lanes (among `valid` ones) holding the same expert id as this lane.
-__device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int nbits) {
-  uint64_t m = __ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(bit);
-    m &= bit ? bb : ~bb;
-  }
-  return m;
-}
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t *__restrict__ ids, int P, int E, int bm, int capacity,
@@ -50,137 +15,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int32_t *__restrict__ block_expert, int32_t *__restrict__ inv_pairs,
     int32_t *__restrict__ n_blocks, WorkItem *__restrict__ items, int32_t *__restrict__ n_items,
     int row_chunk, int T, int S) {
-  __shared__ int cnt[kPermWaves * kMaxExperts];  // per (wave, expert) count, then base
-  __shared__ int tot[kMaxExperts];
-  __shared__ int off[kMaxExperts + 1];
-  __shared__ int item_off[kMaxExperts + 1];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sentinel = P;
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  for (int i = tid; i < kPermWaves * E; i += kPermThreads) cnt[i] = 0;
-  __syncthreads();
-
-  const int per = (P + kPermWaves - 1) / kPermWaves;
-  const int b0 = min(P, wave * per), b1 = min(P, b0 + per);
-  int *my = cnt + wave * E;
-
-  // pass 1: per-wave counts (the slice's ids are fetched kBatch steps at a
-  // time so the loads overlap instead of serialising the walk)
-  for (int base = b0; base < b1; base += kWave * kBatch) {
-    int ev[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = base + u * kWave + lane;
-      ev[u] = p < b1 ? ids[p] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int e = ev[u];
-      const bool valid = e >= 0;
-      const uint64_t m = same_expert_mask(e, valid, nbits);
-      if (valid && __popcll(m & lt_mask) == 0) my[e] += __popcll(m);
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  __syncthreads();
-
-  // exclusive prefix over waves per expert; totals
-  for (int e = tid; e < E; e += kPermThreads) {
-    int s = 0;
-    for (int w = 0; w < kPermWaves; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = s;
-      s += c;
-    }
-    tot[e] = s;
-  }
-  __syncthreads();
-
-  // exclusive scan of padded totals; work-list offsets
-  if (wave == 0) {
-    int run = 0, irun = 0;
-    for (int base = 0; base < E; base += kWave) {
-      const int e = base + lane;
-      const int pad = e < E ? (tot[e] + bm - 1) / bm * bm : 0;
-      const int inc = wave_incl_scan(pad, lane);
-      const int ni = (e < E && row_chunk > 0) ? (pad + row_chunk - 1) / row_chunk : 0;
-      const int iinc = wave_incl_scan(ni, lane);
-      if (e < E) {
-        off[e] = run + inc - pad;
-        item_off[e] = irun + iinc - ni;
-      }
-      run += __shfl(inc, kWave - 1, kWave);
-      irun += __shfl(iinc, kWave - 1, kWave);
-    }
-    if (lane == 0) {
-      off[E] = run;
-      item_off[E] = irun;
-    }
-  }
-  __syncthreads();
-
-  const int total = off[E];
-  const int nb = total / bm;
-  const int nb_cap = (capacity + bm - 1) / bm;
-  for (int e = tid; e <= E; e += kPermThreads) expert_offsets[e] = off[e];
-  if (tid == 0) *n_blocks = nb;
-  for (int e = tid; e < E; e += kPermThreads) {
-    for (int b = off[e] / bm; b < off[e + 1] / bm; ++b) block_expert[b] = e;
-    for (int r = off[e] + tot[e]; r < off[e + 1]; ++r) sorted_pairs[r] = sentinel;
-  }
-  for (int b = nb + tid; b < nb_cap; b += kPermThreads) block_expert[b] = -1;
-  for (int r = total + tid; r < capacity; r += kPermThreads) sorted_pairs[r] = sentinel;
-
-  // work list for the expert stages: routed segments cut into row_chunk rows,
-  // then the shared experts' token rows
-  if (items) {
-    for (int e = tid; e < E; e += kPermThreads) {
-      const int pad = off[e + 1] - off[e];
-      int k = item_off[e];
-      for (int r0 = 0; r0 < pad; r0 += row_chunk, ++k)
-        items[k] = WorkItem{e, off[e] + r0, min(row_chunk, pad - r0), 0};
-    }
-    const int per_shared = (T + row_chunk - 1) / row_chunk;
-    for (int i = tid; i < S * per_shared; i += kPermThreads) {
-      const int s = i / per_shared, c = i % per_shared;
-      const int r0 = c * row_chunk;
-      items[item_off[E] + i] = WorkItem{E + s, capacity + s * T + r0, min(row_chunk, T - r0), 0};
-    }
-    if (tid == 0) *n_items = item_off[E] + S * per_shared;
-  }
-
-  // pass 2: scatter (rows from base + running count + rank in the step)
-  for (int base = b0; base < b1; base += kWave * kBatch) {
-    int ev[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = base + u * kWave + lane;
-      ev[u] = p < b1 ? ids[p] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = base + u * kWave + lane;
-      const int e = ev[u];
-      const bool valid = e >= 0;
-      const uint64_t m = same_expert_mask(e, valid, nbits);
-      if (valid) {
-        const int rank = __popcll(m & lt_mask);
-        const int row = off[e] + my[e] + rank;
-        sorted_pairs[row] = p;
-        inv_pairs[p] = row;
-        // the leader's update is ordered after every lane's read above (same wave)
-        __builtin_amdgcn_wave_barrier();
-        if (rank == 0) my[e] += __popcll(m);
-      } else if (p < b1) {
-        inv_pairs[p] = -1;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  __shared__ int lds[permute_lds_ints<kPermWaves>()];
+  permute_block<kPermWaves>(ids, P, E, bm, capacity, sorted_pairs, expert_offsets, block_expert,
+                            inv_pairs, n_blocks, items, n_items, row_chunk, T, S, lds);
 }
 
 int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int32_t n_shared,

@@ -1,5 +1,6 @@
 // kernels_route.hip -- per-token e4m3 quantisation, fp32 router logits and
-// wave64 top-k with softmax weights, for gfx950.
+// wave64 top-k with softmax weights, for gfx950 (per-stage kernels; the
+// device functions live in route_dev.hpp).
 //
 // Layer statement: "Routage MoE entre GPU" (router paragraph): the router
 // scores every expert from the token's hidden state, keeps the best k and
@@ -7,9 +8,9 @@
 // section.
 #include "common.hpp"
 #include "internal.hpp"
+#include "route_dev.hpp"
 
 namespace fp8moe {
-
 // ------------------------------------------------------------------ quantise
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const float *__restrict__ x, int rows,
                                                             int cols, uint8_t *__restrict__ q,
@@ -39,12 +40,7 @@ hipError_t launch_quantize_rows(const float *x, int32_t rows, int32_t cols, uint
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ router, decode-sized
-// One wave per (token, expert) dot product over d, lanes striding d by 4
-// floats with all of a lane's loads issued before the FMAs.  The wave of
-// expert 0 also quantises its token's row (it has read the row already).
-constexpr int kDotVec = 8;  // float4 per lane per round: d <= 2048 in one round
-
+// ------------------------------------------------------------------ router
 __global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict__ x,
                                                          const float *__restrict__ wr,
                                                          const float *__restrict__ bias, int T,
@@ -53,45 +49,17 @@ __global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict
                                                          float *__restrict__ sx) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid >= T * E) return;
-  const int lane = threadIdx.x & 63;
-  const int t = wid / E, e = wid - t * E;
-  const float *xr = x + (size_t)t * d;
-  const float *w = wr + (size_t)e * d;
-  float acc = 0.0f, amax = 0.0f;
-  for (int base = 0; base < d; base += kDotVec * 256) {
-    v4f xv[kDotVec], wv[kDotVec];
-#pragma unroll
-    for (int j = 0; j < kDotVec; ++j) {
-      const int i = base + (j * 64 + lane) * 4;
-      xv[j] = i < d ? *reinterpret_cast<const v4f *>(xr + i) : v4f{0.f, 0.f, 0.f, 0.f};
-      wv[j] = i < d ? *reinterpret_cast<const v4f *>(w + i) : v4f{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int j = 0; j < kDotVec; ++j) {
-      acc = fmaf(xv[j].x, wv[j].x, acc);
-      acc = fmaf(xv[j].y, wv[j].y, acc);
-      acc = fmaf(xv[j].z, wv[j].z, acc);
-      acc = fmaf(xv[j].w, wv[j].w, acc);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv[j].x), fabsf(xv[j].y)),
-                               fmaxf(fabsf(xv[j].z), fabsf(xv[j].w))));
-    }
-  }
-  acc = wave_sum(acc);
-  if (lane == 0) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
-  if (e == 0 && xq) {
-    amax = wave_max(amax);
-    float r = 1.0f, s = 1.0f;
-    if (amax != 0.0f) {
-      r = kE4m3Max / amax;
-      s = amax / kE4m3Max;
-    }
-    uint8_t *q = xq + (size_t)t * d;
-    for (int i = lane * 4; i < d; i += kWave * 4) {
-      const v4f v = *reinterpret_cast<const v4f *>(xr + i);
-      *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x * r, v.y * r, v.z * r, v.w * r);
-    }
-    if (lane == 0) sx[t] = s;
-  }
+  const int t = wid / E;
+  router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, wid - t * E, threadIdx.x & 63);
+}
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const float *__restrict__ x,
+                                                          const float *__restrict__ wr,
+                                                          const float *__restrict__ bias, int T,
+                                                          int d, int E, float *__restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) float lds[kRouterTileLdsFloats];
+  router_tile(x, wr, bias, T, d, E, logits, blockIdx.x * kRT, blockIdx.y * kRE, lds,
+              lds + kRT * kRS);
 }
 
 hipError_t launch_route_logits(const float *x, const float *w_router, const float *bias, int32_t T,
@@ -108,81 +76,6 @@ hipError_t launch_route_logits(const float *x, const float *w_router, const floa
   return launch_router(x, w_router, bias, T, d, E, logits, stream);
 }
 
-// ------------------------------------------------------------------ router, tiled
-// Batches with many (token, expert) pairs: logits = X . W_r^T as an fp32
-// GEMM on v_mfma_f32_16x16x4_f32.  A workgroup computes 32 tokens x 64
-// experts; K advances 64 floats at a time through LDS (rows padded to 68
-// floats so the per-lane reads hit distinct banks), the next chunk's global
-// loads in flight while the current one is multiplied.  Wave w owns tokens
-// [16*(w&1), +16) x experts [32*(w>>1), +32): two 16x16 tiles.
-constexpr int kRT = 32, kRE = 64, kRK = 64, kRS = kRK + 4;
-
-__global__ __launch_bounds__(256) void router_mfma_kernel(const float *__restrict__ x,
-                                                          const float *__restrict__ wr,
-                                                          const float *__restrict__ bias, int T,
-                                                          int d, int E, float *__restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) float xs[kRT * kRS];
-  __shared__ __attribute__((aligned(16))) float ws[kRE * kRS];
-  const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int th = wave & 1, eh = wave >> 1;
-  const int lr = lane & 15, lk = lane >> 4;
-  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  // the next K chunk is fetched into registers while the current one is used
-  constexpr int XJ = kRT * kRK / 4 / 256, WJ = kRE * kRK / 4 / 256;
-  v4f xr[XJ], wrg[WJ];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < XJ; ++j) {
-      const int i = tid + j * 256, r = i >> 4, c = (i & 15) * 4;
-      xr[j] = t0 + r < T ? *reinterpret_cast<const v4f *>(x + (size_t)(t0 + r) * d + k0 + c)
-                         : v4f{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int i = tid + j * 256, r = i >> 4, c = (i & 15) * 4;
-      wrg[j] = e0 + r < E ? *reinterpret_cast<const v4f *>(wr + (size_t)(e0 + r) * d + k0 + c)
-                          : v4f{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  fetch(0);
-  for (int k0 = 0; k0 < d; k0 += kRK) {
-#pragma unroll
-    for (int j = 0; j < XJ; ++j) {
-      const int i = tid + j * 256;
-      *reinterpret_cast<v4f *>(xs + (i >> 4) * kRS + (i & 15) * 4) = xr[j];
-    }
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      const int i = tid + j * 256;
-      *reinterpret_cast<v4f *>(ws + (i >> 4) * kRS + (i & 15) * 4) = wrg[j];
-    }
-    __syncthreads();
-    if (k0 + kRK < d) fetch(k0 + kRK);
-    const float *xa = xs + (16 * th + lr) * kRS + lk;
-    const float *wb0 = ws + (32 * eh + lr) * kRS + lk;
-    const float *wb1 = wb0 + 16 * kRS;
-#pragma unroll
-    for (int kk = 0; kk < kRK; kk += 4) {
-      const float a = xa[kk];
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, wb0[kk], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, wb1[kk], acc[1], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int e = e0 + 32 * eh + 16 * n + lr;
-    if (e >= E) continue;
-    const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * th + 4 * lk + i;
-      if (t < T) logits[(size_t)t * E + e] = bias ? acc[n][i] + b : acc[n][i];
-    }
-  }
-}
-
 hipError_t launch_router(const float *x, const float *w_router, const float *bias, int32_t T,
                          int32_t d, int32_t E, float *logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
@@ -197,62 +90,13 @@ hipError_t launch_router(const float *x, const float *w_router, const float *bia
 }
 
 // ------------------------------------------------------------------ top-k
-// One wave per token.  Each expert becomes a 64-bit key: the logit's bits
-// mapped to an unsigned order (with -0 folded onto +0) in the high word and
-// 0xFFFF - e in the low word, so the largest key is the largest logit with
-// the lowest index.  k_t rounds of a wave-wide max pick the slots in order;
-// the softmax over the picked logits is accumulated in slot order.
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
-  uint32_t b = __float_as_uint(l);
-  if ((b & 0x7fffffffu) == 0) b = 0;  // -0 == +0
-  uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFF - e);
-}
-
-constexpr int kTopkSlots = kMaxExperts / kWave;
-
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k_max, const int32_t *__restrict__ kpt,
                                                    int32_t *__restrict__ ids,
                                                    float *__restrict__ w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int lane = threadIdx.x & 63;
-  const float *l = logits + (size_t)t * E;
-  uint64_t key[kTopkSlots];
-#pragma unroll
-  for (int c = 0; c < kTopkSlots; ++c) {
-    int e = lane + c * kWave;
-    key[c] = e < E ? route_key(l[e], e) : 0ull;
-  }
-  const int kt = kpt ? kpt[t] : k_max;
-  float m = 0.0f, z = 0.0f, my_eps = 0.0f;
-  int my_id = -1;
-  for (int j = 0; j < kt; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int c = 0; c < kTopkSlots; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_u64(best);
-    const int e = 0xFFFF - (int)(best & 0xFFFFu);
-    const float lv = l[e];
-    if (j == 0) m = lv;
-    const float eps = expf(lv - m);
-    z += eps;
-    if (lane == j) {
-      my_eps = eps;
-      my_id = e;
-    }
-    if ((e & 63) == lane) {
-#pragma unroll
-      for (int c = 0; c < kTopkSlots; ++c)
-        if (c == (e >> 6)) key[c] = 0ull;
-    }
-  }
-  if (lane < k_max) {
-    const size_t o = (size_t)t * k_max + lane;
-    ids[o] = lane < kt ? my_id : -1;
-    w[o] = lane < kt ? my_eps / z : 0.0f;
-  }
+  topk_token_wave(logits, T, E, k_max, kpt, ids, w, t, threadIdx.x & 63);
 }
 
 hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,

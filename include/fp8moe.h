@@ -67,8 +67,13 @@ enum {
 };
 
 enum {
-  MOE_F_NO_REQUANT = 1u << 0 /* keep SiLU*up in fp32 and run the down projection on fp32
-                                products; an accuracy mode, not a fast path */
+  MOE_F_NO_REQUANT = 1u << 0, /* keep SiLU*up in fp32 and run the down projection on fp32
+                                 products; an accuracy mode, not a fast path */
+  MOE_F_PERSISTENT = 1u << 1  /* reserved for running moe_fused_forward as one cooperative
+                                 launch (the fused single kernel of the Alpha-MoE article,
+                                 section "Comment fonctionne le megakernel").  Switched off in
+                                 this build: moe_fused_forward returns MOE_ERR_UNSUPPORTED
+                                 when it is set */
 };
 
 /* Limits checked by every call. */

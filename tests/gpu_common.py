@@ -64,8 +64,9 @@ class Layer:
                                               host.get("ws_down"))
             del host
 
-    def layer(self, block_m=16, no_requant=False):
-        return lib().MoELayer(self.dw, self.w_router, self.spec.k, self.bias, block_m, no_requant)
+    def layer(self, block_m=16, no_requant=False, persistent=False):
+        return lib().MoELayer(self.dw, self.w_router, self.spec.k, self.bias, block_m, no_requant,
+                              persistent)
 
 
 def rel_l2(a, b) -> float:

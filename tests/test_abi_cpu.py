@@ -107,6 +107,12 @@ def test_fused_forward_rejects_null_and_alignment_and_workspace():
     bad_flags = _dims()
     bad_flags.flags = 1 << 5
     assert call(dims=bad_flags) == ERR_UNSUPPORTED
+    # the single-launch flag is switched off: refused before any launch
+    for extra in (0, fp8.MOE_F_NO_REQUANT):
+        pers = _dims()
+        pers.flags = fp8.MOE_F_PERSISTENT | extra
+        assert call(dims=pers) == ERR_UNSUPPORTED
+        assert b"switched off" in fp8._last_error()
 
 
 def test_step_entry_points_reject_bad_arguments():

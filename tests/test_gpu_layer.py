@@ -24,13 +24,14 @@ TOL_REQUANT = 2e-2
 TOL_NO_REQUANT = 1e-3
 
 
-def _check(L: Layer, T=None, no_requant=False, sample=None, block_m=16, seed=0, equal=False):
+def _check(L: Layer, T=None, no_requant=False, sample=None, block_m=16, seed=0, equal=False,
+           persistent=False):
     """Run the GPU layer on the first T tokens; compare (a sample of) rows."""
     spec = L.spec
     T = spec.T if T is None else T
     x = L.x[:T].contiguous()
     kpt = None if L.kpt is None else L.kpt[:T].contiguous()
-    layer = L.layer(block_m=block_m, no_requant=no_requant)
+    layer = L.layer(block_m=block_m, no_requant=no_requant, persistent=persistent)
     m = lib()
     if equal:
         logits = torch.zeros((T, spec.E), dtype=torch.float32, device=dev())
@@ -114,6 +115,34 @@ def test_deterministic_and_batch_invariant(small):
     assert rel_l2(to_np(c), to_np(a)[to_np(sub)]) < 1e-6
 
 
+PERSISTENT_OFF = ("single-launch path switched off: its cooperative launch did not complete "
+                  "on gfx950 under test (grid barrier never released); cause not established")
+
+
+@pytest.mark.skip(reason=PERSISTENT_OFF)
+def test_persistent_single_launch_matches_staged(small):
+    """One cooperative launch runs the same stage functions as the seven
+    per-stage kernels: outputs and routing must be bit-identical, and within
+    the bar against the oracle."""
+    _check(small, persistent=True)
+    staged = small.layer()
+    pers = small.layer(persistent=True)
+    ids_a = torch.empty((small.spec.T, small.spec.k), dtype=torch.int32, device=dev())
+    ids_b = torch.empty_like(ids_a)
+    a = staged.forward(small.x, k_per_token=small.kpt, topk_ids=ids_a)
+    b = pers.forward(small.x, k_per_token=small.kpt, topk_ids=ids_b)
+    b2 = pers.forward(small.x, k_per_token=small.kpt)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_b)
+    assert torch.equal(a, b) and torch.equal(b, b2)
+
+
+def test_persistent_flag_is_refused(small):
+    for nr in (False, True):
+        with pytest.raises(lib().MoEError):
+            small.layer(no_requant=nr, persistent=True).forward(small.x, k_per_token=small.kpt)
+
+
 # ----------------------------------------------------------------- full-size layers, sampled
 
 def test_mixtral_decode_sweep():
@@ -148,3 +177,16 @@ def test_prism_elastic_k():
     err = _check(L, sample=8, seed=3)
     print(f"prism T=1024 rel-L2 {err:.3e}")
     _check(L, sample=4, seed=4, no_requant=True)
+
+
+@pytest.mark.skip(reason=PERSISTENT_OFF)
+def test_persistent_full_size():
+    L = Layer(wl.MIXTRAL)
+    for T in (1, 256):
+        _check(L, T=T, sample=4, seed=T + 1, persistent=True)
+    del L
+    L = Layer(wl.QWEN3.with_(T=4096))
+    _check(L, T=4096, sample=4, seed=5, persistent=True)
+    del L
+    L = Layer(wl.PRISM)
+    _check(L, sample=4, seed=6, persistent=True)
