@@ -54,6 +54,8 @@ def _sig(name, restype, *argtypes):
 _DP = C.POINTER(Dims)
 _WP = C.POINTER(_Weights)
 _quantize_rows = _sig("moe_quantize_rows", _i32, _vp, _i32, _i32, _vp, _vp, _vp)
+_packed_weight_bytes = _sig("moe_packed_weight_bytes", C.c_int64, _i32, _i32)
+_pack_weights = _sig("moe_pack_weights", _i32, _vp, _i32, _i32, _vp, _vp)
 _router_logits = _sig("moe_router_logits", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _route_topk = _sig("moe_route_topk", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 _capacity = _sig("moe_capacity", C.c_int64, _i32, _i32, _i32, _i32)
@@ -128,6 +130,30 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None, scale=None,
     return q, scale
 
 
+def packed_weight_bytes(rows: int, cols: int) -> int:
+    """Bytes of a [rows][cols] code matrix in tile order (0 for bad shapes)."""
+    return int(_packed_weight_bytes(rows, cols))
+
+
+def packed_shape(rows: int, cols: int):
+    """Tensor shape used for one tile-order matrix: [rows/16, ceil(cols/128), 2048]."""
+    return (rows // 16, (cols + 127) // 128, 2048)
+
+
+def pack_weights(codes: torch.Tensor, packed: Optional[torch.Tensor] = None, stream=None):
+    """Row-major e4m3 codes [rows][cols] -> tile order (the layout the
+    expert GEMMs read; see moe_weights in include/fp8moe.h)."""
+    rows, cols = codes.shape
+    if packed is None:
+        packed = torch.empty(packed_shape(rows, cols), dtype=torch.uint8, device=codes.device)
+    need = packed_weight_bytes(rows, cols)  # 0: a bad shape, reported by the library
+    if need and packed.numel() != need:
+        raise ValueError(f"packed holds {packed.numel()} bytes, {need} needed")
+    _check(_pack_weights(_ptr(codes, torch.uint8), rows, cols, _ptr(packed, torch.uint8),
+                         _stream(stream)))
+    return packed
+
+
 def router_logits(x, w_router, bias=None, stream=None):
     T, d = x.shape
     E = w_router.shape[0]
@@ -168,12 +194,14 @@ def permute(topk_ids, E: int, block_m: int, cap: Optional[int] = None, stream=No
 
 @dataclass
 class DeviceWeights:
-    """e4m3 expert weights (uint8 codes) with fp32 per-output-channel scales."""
-    w_gate: torch.Tensor  # [E, f, d]
+    """e4m3 expert weights with fp32 per-output-channel scales.  The codes are
+    kept in tile order (pack_weights): one [f/16, ceil(d/128), 2048] block per
+    expert for gate and up, [d/16, ceil(f/128), 2048] for down."""
+    w_gate: torch.Tensor  # [E, f/16, ceil(d/128), 2048]
     w_up: torch.Tensor
     s_gate: torch.Tensor  # [E, f]
     s_up: torch.Tensor
-    w_down: torch.Tensor  # [E, d, f]
+    w_down: torch.Tensor  # [E, d/16, ceil(f/128), 2048]
     s_down: torch.Tensor  # [E, d]
     ws_gate: Optional[torch.Tensor] = None
     ws_up: Optional[torch.Tensor] = None
@@ -188,11 +216,11 @@ class DeviceWeights:
 
     @property
     def f(self) -> int:
-        return int(self.w_gate.shape[1])
+        return int(self.s_gate.shape[1])
 
     @property
     def d(self) -> int:
-        return int(self.w_gate.shape[2])
+        return int(self.s_down.shape[1])
 
     @property
     def n_shared(self) -> int:
@@ -206,19 +234,22 @@ class DeviceWeights:
 
     @staticmethod
     def empty(E: int, d: int, f: int, n_shared: int = 0, device="cuda") -> "DeviceWeights":
-        u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=device)
+        u8 = lambda n, r, c: torch.empty((n,) + packed_shape(r, c), dtype=torch.uint8, device=device)
         f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=device)
         w = DeviceWeights(u8(E, f, d), u8(E, f, d), f32(E, f), f32(E, f), u8(E, d, f), f32(E, d))
         if n_shared:
-            w.ws_gate, w.ws_up, w.ws_down = u8(n_shared, f, d), u8(n_shared, f, d), u8(n_shared, d, f)
-            w.ss_gate, w.ss_up, w.ss_down = f32(n_shared, f), f32(n_shared, f), f32(n_shared, d)
+            S = n_shared
+            w.ws_gate, w.ws_up, w.ws_down = u8(S, f, d), u8(S, f, d), u8(S, d, f)
+            w.ss_gate, w.ss_up, w.ss_down = f32(S, f), f32(S, f), f32(S, d)
         return w
 
     def set_expert(self, which: str, e: int, w32: torch.Tensor, shared: bool = False):
-        """Quantise one fp32 expert matrix per output channel into slot e."""
+        """Quantise one fp32 expert matrix [rows][cols] per output channel and
+        store it in tile order in slot e."""
         pre = "ws_" if shared else "w_"
         spre = "ss_" if shared else "s_"
-        quantize_rows(w32.contiguous(), getattr(self, pre + which)[e], getattr(self, spre + which)[e])
+        codes, _ = quantize_rows(w32.contiguous(), scale=getattr(self, spre + which)[e])
+        pack_weights(codes, getattr(self, pre + which)[e])
 
 
 # --------------------------------------------------------------------------- expert stages

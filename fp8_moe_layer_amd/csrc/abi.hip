@@ -111,26 +111,67 @@ int32_t choose_msub(const moe_dims *d) {
   return m;
 }
 
-// K splits of the down projection: enough workgroups to keep every CU
-// streaming when few experts are active (decode), one split otherwise.
-int32_t choose_down_splits(const moe_dims *d, int32_t msub) {
-  if (d->flags & MOE_F_NO_REQUANT) return 1;
-  const int forced = env_int("FP8MOE_DOWN_SPLITS", 0);  // tile-tuning override
-  if (forced > 0) return down_splits_used(d->f, msub, forced);
+// Experts expected to receive at least one token (uniform routing).
+double expected_active(const moe_dims *d) {
   const double E = d->E;
-  const double active = E * (1.0 - pow(1.0 - (double)d->k_max / E, (double)d->T)) + d->n_shared;
-  const double tiles = (d->d + kDownChannels - 1) / kDownChannels;
-  int32_t s = (int32_t)ceil(1024.0 / (active * tiles));
-  if (s < 1) s = 1;
-  if (s > 8) s = 8;
-  return down_splits_used(d->f, msub, s);
+  return E * (1.0 - pow(1.0 - (double)d->k_max / E, (double)d->T));
+}
+
+// Expected work items of the grouped GEMMs (rows cut into 16*msub chunks).
+double expected_items(const moe_dims *d, int32_t msub) {
+  const double chunk = 16.0 * msub;
+  const double rows = (double)d->T * d->k_max / d->E + d->block_m - 1;
+  const double per = rows > chunk ? ceil(rows / chunk) : 1.0;
+  return expected_active(d) * per + d->n_shared * ceil(d->T / chunk);
+}
+
+// Grouped-GEMM geometry.  A workgroup of W compute waves covers
+// W * ch_wave output channels; up to five compute waves two workgroups
+// share a CU, more make one per CU.  The work is a whole number of rounds
+// of resident workgroups, so W is chosen to waste least of the last round
+// and of partial channel tiles: efficiency = (workgroups / (rounds * slots))
+// * (N / (tiles * W * ch_wave)), ties to the larger W (fewer activation
+// re-reads).  K splits (down only) aim at two rounds.
+struct GemmPlan {
+  int32_t waves, splits;
+};
+
+constexpr int kCUs = 256;
+
+GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
+  const double items = expected_items(d, msub);
+  const int N = gate_up ? d->f : d->d;
+  const int ch_wave = gate_up ? 16 : kDownChannelsPerWave;
+  const int forced = env_int("FP8MOE_WAVES", 0);  // tile-tuning override
+  GemmPlan best{4, 1};
+  double best_eff = -1.0;
+  for (int W = kGemmMaxWaves; W >= 3; --W) {
+    if (forced >= 1 && forced <= kGemmMaxWaves && W != forced) continue;
+    const double slots = (double)kCUs * (W <= 5 ? 2 : 1);
+    const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);
+    int32_t splits = 1;
+    if (!gate_up && !(d->flags & MOE_F_NO_REQUANT)) {
+      const int want = (int)ceil(2.0 * slots / (items * tiles));
+      splits = down_splits_used(d->f, msub, want < 1 ? 1 : want > 8 ? 8 : want);
+    }
+    const double n = items * tiles * splits;
+    const double rounds = ceil(n / slots);
+    const double eff = (n / (rounds * slots)) * ((double)N / ((double)tiles * W * ch_wave));
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = GemmPlan{W, splits};
+    }
+  }
+  const int fs = env_int("FP8MOE_DOWN_SPLITS", 0);  // tile-tuning override
+  if (!gate_up && fs > 0 && !(d->flags & MOE_F_NO_REQUANT)) best.splits = down_splits_used(d->f, msub, fs);
+  return best;
 }
 
 // Workspace layout of moe_fused_forward (all pieces 256-byte aligned).
 struct Layout {
   size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
       hq, sh, y, total;
-  int32_t capacity, rows_total, max_items, row_chunk, msub, splits;
+  int32_t capacity, rows_total, max_items, row_chunk, msub, splits, waves_gu, waves_dn;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -141,7 +182,10 @@ Layout layout_of(const moe_dims *d) {
   L.rows_total = L.capacity + d->n_shared * d->T;
   L.msub = choose_msub(d);
   L.row_chunk = 16 * L.msub;
-  L.splits = choose_down_splits(d, L.msub);
+  L.waves_gu = plan_gemm(d, L.msub, true).waves;
+  const GemmPlan dn = plan_gemm(d, L.msub, false);
+  L.waves_dn = dn.waves;
+  L.splits = dn.splits;
   L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
   const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
   size_t o = 0;
@@ -217,6 +261,27 @@ moe_status moe_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t
   if (!aligned(x, 16) || !aligned(q, 4) || !aligned(scale, 4))
     return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte and q 4-byte aligned", fn);
   moe_status s = hip_status(launch_quantize_rows(x, rows, cols, q, scale, as_stream(stream)), fn);
+  return s ? s : ok();
+}
+
+int64_t moe_packed_weight_bytes(int32_t rows, int32_t cols) {
+  if (rows <= 0 || rows % 16 || cols <= 0 || cols % 64) return 0;
+  return (int64_t)rows * ((cols + 127) / 128) * 128;
+}
+
+moe_status moe_pack_weights(const uint8_t *codes, int32_t rows, int32_t cols, uint8_t *packed,
+                            void *stream) {
+  const char *fn = "moe_pack_weights";
+  if (!codes || !packed) return fail(MOE_ERR_NULL, "%s: codes and packed are required", fn);
+  if (moe_packed_weight_bytes(rows, cols) == 0 || cols > MOE_MAX_FFN)
+    return fail(MOE_ERR_SHAPE, "%s: rows=%d cols=%d (rows a multiple of 16, cols of 64 up to %d)",
+                fn, rows, cols, MOE_MAX_FFN);
+  if (!aligned(codes, 16) || !aligned(packed, 16))
+    return fail(MOE_ERR_ALIGN, "%s: codes and packed must be 16-byte aligned", fn);
+  const uintptr_t a = (uintptr_t)codes, b = (uintptr_t)packed;
+  const uintptr_t na = (uintptr_t)rows * cols, nb = (uintptr_t)moe_packed_weight_bytes(rows, cols);
+  if (a < b + nb && b < a + na) return fail(MOE_ERR_SHAPE, "%s: codes and packed overlap", fn);
+  moe_status s = hip_status(launch_pack_weights(codes, rows, cols, packed, as_stream(stream)), fn);
   return s ? s : ok();
 }
 
@@ -305,7 +370,10 @@ moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint
   if (!xq || !sx || !h) return fail(MOE_ERR_NULL, "%s: xq, sx and h are required", fn);
   if (!aligned(xq, 16)) return fail(MOE_ERR_ALIGN, "%s: xq must be 16-byte aligned", fn);
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
-  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, choose_msub(dims), as_stream(stream)), fn);
+  const int32_t msub = choose_msub(dims);
+  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub,
+                                plan_gemm(dims, msub, true).waves, as_stream(stream)),
+                 fn);
   return s ? s : ok();
 }
 
@@ -323,8 +391,9 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
   if ((f32 && !aligned(h, 16)) || (!f32 && !aligned(hq, 16)))
     return fail(MOE_ERR_ALIGN, "%s: the activation rows must be 16-byte aligned", fn);
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
+  const int32_t msub = choose_msub(dims);
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
-                             choose_msub(dims), 1, as_stream(stream)),
+                             msub, 1, plan_gemm(dims, msub, false).waves, as_stream(stream)),
                  fn);
   return s ? s : ok();
 }
@@ -427,16 +496,18 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   rs.max_items = L.max_items;
   const ExpertWeights ew = to_internal(w);
   mark(3);
-  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, st), "gate_up"))) return s;
+  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.waves_gu, st), "gate_up"))) return s;
   mark(4);
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, st), "down")))
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, L.waves_dn, st),
+                        "down")))
       return s;
   } else {
     mark(5);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, st), "down"))) return s;
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, L.waves_dn, st), "down")))
+      return s;
   }
   mark(6);
   if ((s = hip_status(launch_combine(rs, y, L.splits, ids, tw, inv, out, st), "combine"))) return s;

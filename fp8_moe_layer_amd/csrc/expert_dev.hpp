@@ -27,9 +27,10 @@
 //
 // MFMA operand layout (same for A = activation rows and B = weight rows):
 // lane l holds row l%16 and, of each 128-byte K step, the bytes
-// [16*(l/16), +16) and [64 + 16*(l/16), +16).  Each 16-byte piece load of a
-// wave then covers 16 rows x 64 contiguous bytes.  Result tile: lane l,
-// element i = C[4*(l/16) + i][l%16].
+// [16*(l/16), +16) and [64 + 16*(l/16), +16).  The weights are stored in
+// that order (tile order, moe_weights), so each weight piece load of a wave
+// is 1 KB contiguous; an activation piece load covers 16 rows x 64 bytes.
+// Result tile: lane l, element i = C[4*(l/16) + i][l%16].
 #pragma once
 #include "common.hpp"
 #include "internal.hpp"
@@ -109,6 +110,15 @@ struct Chunk {
   static constexpr int PF = MSUB <= 2 ? 4 : 2;
 };
 
+// LDS of a grouped-GEMM workgroup: the activation ring, then a table of the
+// activation scale of each row of the current row pass (two copies by pass
+// parity), 0 for a padding row.  The loader wave fills the table with the
+// same row lookups it makes for the gather, so the epilogue needs no global
+// loads on its critical path.
+constexpr int kGemmRingBytes = Chunk<1>::NBUF * Chunk<1>::BYTES;
+constexpr int kGemmRowTable = 2 * 16 * 8;  // floats: two passes of up to 128 rows
+constexpr int kGemmLdsBytes = kGemmRingBytes + kGemmRowTable * (int)sizeof(float);
+
 // s_waitcnt vmcnt(n * 16): n chunks of loads may stay in flight.
 __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
   if (chunks_in_flight >= 2)
@@ -122,10 +132,13 @@ __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
 // GATEUP: out = h[rows][f], NB must be 2 (gate row, up row of the same channel).
 // else:   out = y[split][rows][d], NB channel groups of 16 per wave.
 // One call computes tile `bid` (= (item * n_tiles + tile) * splits + split)
-// with a workgroup of 5 waves (4 compute + 1 loader); abuf: 64 KB of LDS,
-// 1024-byte aligned.  Returns early (uniformly) for an empty item.
+// with a workgroup of W = blockDim.x/64 - 1 compute waves (1..8) and one
+// loader wave (wave W); the tile is W * 16 * (GATEUP ? 1 : NB) output
+// channels wide.  abuf: kGemmLdsBytes of LDS, 1024-byte aligned.  Returns
+// early (uniformly) for an empty item.
 template <int MSUB, int NB, bool GATEUP>
 __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t *abuf) {
+  const int W = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6) - 1);  // compute waves
   using C = Chunk<MSUB>;
   static_assert(C::LPC == 16 && C::NBUF == 4, "loader_wait_barrier assumes 16 loads per chunk");
 
@@ -133,7 +146,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   const int K = GATEUP ? rs.d : rs.f;
   const int N = GATEUP ? rs.f : rs.d;
   constexpr int CH_WAVE = GATEUP ? 16 : 16 * NB;
-  constexpr int CH_WG = 4 * CH_WAVE;
+  const int CH_WG = W * CH_WAVE;
   const int n_tiles = (N + CH_WG - 1) / CH_WG;
   const int split = bid % g.splits;
   bid /= g.splits;
@@ -149,7 +162,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   // activation pieces by a repeat of the last weight step.
   const int nks_pf = (nks + C::PF - 1) / C::PF * C::PF;
   const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;  // LDS chunks of KSC steps
-  const bool half_tail = (k_end - k_begin) & 127;       // last step holds 64 bytes
+  const int KT = (K + 127) >> 7;                        // weight tiles along K
 
   const bool shared = expert >= rs.E;
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
@@ -157,26 +170,38 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kg = lane >> 4;
 
-  if (wave == 4) {
+  float *row_scale = reinterpret_cast<float *>(abuf + kGemmRingBytes);
+
+  if (wave == W) {
     // ---------------- loader wave: activation rows -> LDS, chunk by chunk
     const uint8_t *abase[MSUB];
-    for (int p0 = 0; p0 < rows; p0 += C::MP) {
+    int pass = 0;
+    for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
       const int prow = min(C::MP, rows - p0);
       const int msub = (prow + 15) >> 4;
+      float *rsc = row_scale + (pass & 1) * 128;
 #pragma unroll
       for (int m = 0; m < MSUB; ++m) {
         const int r = p0 + m * 16 + ln;
         const uint8_t *b = nullptr;
+        float sc = 0.0f;
         if (m < msub && r < rows) {
           if (GATEUP) {
             const int tok = row_token(rs, row0 + r);
-            if (tok >= 0) b = g.a + (size_t)tok * K;
+            if (tok >= 0) {
+              b = g.a + (size_t)tok * K;
+              sc = g.a_scale[tok];
+            }
           } else if (row_real(rs, row0 + r)) {
             b = g.a + (size_t)(row0 + r) * K;
+            sc = g.a_scale[row0 + r];
           }
         }
         abase[m] = b;
+        if (kg == 0) rsc[m * 16 + ln] = sc;
       }
+      // the table is complete before the first barrier of the pass
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       auto issue = [&](int c) {
         uint8_t *dst = abuf + (c % C::NBUF) * C::BYTES;
 #pragma unroll
@@ -216,22 +241,23 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
     if (GATEUP) {
       o = tile * CH_WG + wave * 16 + ln;
       wbase = (nb == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
-              ex * (size_t)N * K;
+              ex * (size_t)N * KT * 128;
     } else {
       o = tile * CH_WG + wave * CH_WAVE + nb * 16 + ln;
-      wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * K;
+      wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * KT * 128;
     }
     ch[nb] = o;
     const int orow = o < N ? o : N - 1;  // a partial last tile re-reads a valid row
-    bw[nb] = wbase + (size_t)orow * K + k_begin + kg * 16;
+    // tile order: 16 rows x 128 K bytes per 2 KB tile, lane l at l*16 and 1024 + l*16
+    bw[nb] = wbase + ((size_t)(orow >> 4) * KT + (k_begin >> 7)) * 2048 + lane * 16;
   }
-  // Weight pieces of k step ks: +ks*128 and +ks*128+64.  Past the end the step
-  // is clamped to the last one; in a 64-byte tail step the second piece
-  // repeats the first (its activation piece is zero).
+  // Weight tile of k step ks: two contiguous 1 KB halves.  Past the end the
+  // step is clamped to the last one (its activation pieces are zero); the
+  // zero padding of a 64-byte tail step meets zero activation pieces.
   auto load_b = [&](v8i (&b)[NB], int ks) {
     ks = min(ks, nks - 1);
-    const int o0 = ks * 128;
-    const int o1 = (half_tail && ks == nks - 1) ? o0 : o0 + 64;
+    const int o0 = ks * 2048;
+    const int o1 = o0 + 1024;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const v4i lo = load16(bw[nb] + o0);
@@ -243,9 +269,11 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   v8i ring[C::PF][NB];
   v4f acc[MSUB][NB];
   const uint8_t *lds_lane = abuf + lane * 16;
-  for (int p0 = 0; p0 < rows; p0 += C::MP) {
+  int pass = 0;
+  for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
     const int prow = min(C::MP, rows - p0);
     const int msub = (prow + 15) >> 4;
+    const float *rsc = row_scale + (pass & 1) * 128;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
@@ -278,31 +306,30 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
     // ---------------- epilogue
     if (GATEUP) {
       const int o = ch[0];
-      const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + o];
-      const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + o];
+      const bool live = o < N;  // a partial last tile computes a clamped row
+      const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + (live ? o : N - 1)];
+      const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + (live ? o : N - 1)];
 #pragma unroll
       for (int m = 0; m < MSUB; ++m) {
         if (m < msub) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = p0 + m * 16 + kg * 4 + i;
-            if (r < rows) {
-              const int grow = row0 + r;
-              const int tok = row_token(rs, grow);
-              float hv = 0.0f;
-              if (tok >= 0) {
-                const float sxt = g.a_scale[tok];
-                const float gv = acc[m][0][i] * sxt * sgo;
-                const float uv = acc[m][1][i] * sxt * suo;
-                hv = gv / (1.0f + expf(-gv)) * uv;
-              }
-              g.out[(size_t)grow * N + o] = hv;
+            if (r < rows && live) {
+              // a padding row has scale 0 (and zero activations): h = 0
+              const float sxt = rsc[m * 16 + kg * 4 + i];
+              const float gv = acc[m][0][i] * sxt * sgo;
+              const float uv = acc[m][1][i] * sxt * suo;
+              g.out[(size_t)(row0 + r) * N + o] = gv / (1.0f + expf(-gv)) * uv;
             }
           }
         }
       }
     } else {
       const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * N;
+      float sdv[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sdv[nb] = sd[ch[nb] < N ? ch[nb] : N - 1];
       float *ys = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N;
 #pragma unroll
       for (int m = 0; m < MSUB; ++m) {
@@ -311,12 +338,12 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
           for (int i = 0; i < 4; ++i) {
             const int r = p0 + m * 16 + kg * 4 + i;
             if (r < rows) {
+              // a padding row has scale 0 (and zero activations): y = 0
+              const float shr = rsc[m * 16 + kg * 4 + i];
               const int grow = row0 + r;
-              const bool real = row_real(rs, grow);
-              const float shr = real ? g.a_scale[grow] : 0.0f;
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) {
-                if (ch[nb] < N) ys[(size_t)grow * N + ch[nb]] = real ? acc[m][nb][i] * shr * sd[ch[nb]] : 0.0f;
+                if (ch[nb] < N) ys[(size_t)grow * N + ch[nb]] = acc[m][nb][i] * shr * sdv[nb];
               }
             }
           }
@@ -326,7 +353,6 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   }
 }
 
-constexpr int kGemmLdsBytes = Chunk<1>::NBUF * Chunk<1>::BYTES;
 
 // ------------------------------------------------------------------ requant
 // A workgroup of NT threads requantises one real expert row:

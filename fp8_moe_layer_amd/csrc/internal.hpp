@@ -35,6 +35,9 @@ struct RowSpace {
   int32_t max_items;              // grid bound (with items)
 };
 
+// Row-major e4m3 codes [rows][cols] -> tile order (moe_weights).
+hipError_t launch_pack_weights(const uint8_t *codes, int32_t rows, int32_t cols, uint8_t *packed,
+                               hipStream_t stream);
 hipError_t launch_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t *q,
                                 float *scale, hipStream_t stream);
 hipError_t launch_router(const float *x, const float *w_router, const float *bias, int32_t T,
@@ -57,8 +60,13 @@ hipError_t launch_permute(const int32_t *ids, int32_t T, int32_t E, int32_t k_ma
 int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int32_t n_shared,
                        int32_t row_chunk);
 
+// waves: compute waves per workgroup of the grouped GEMMs (1..8; with up to
+// five, two workgroups share a CU).
+constexpr int kGemmMaxWaves = 8;
+constexpr int kGemmMaxThreads = (kGemmMaxWaves + 1) * 64;
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
-                          const ExpertWeights &w, float *h, int32_t msub, hipStream_t stream);
+                          const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
+                          hipStream_t stream);
 // Per-row e4m3 requantisation of h (real rows only): hq codes, sh = amax/448.
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream);
@@ -68,14 +76,14 @@ hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float
 // count actually used is down_splits_used(f, msub, splits).
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
-                       hipStream_t stream);
+                       int32_t waves, hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
 // K bytes per LDS chunk of the grouped GEMMs for a row-pass size.
 int32_t chunk_bytes(int32_t msub);
 // Final K-split count and bytes per split for a requested split count.
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
                          int32_t *ksplit);
-constexpr int kDownChannels = 128;  // output channels per down-projection workgroup
+constexpr int kDownChannelsPerWave = 32;  // output channels per down-projection wave
 // out from y slabs summed in split order.
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
                           const float *w, const int32_t *inv_pairs, float *out,

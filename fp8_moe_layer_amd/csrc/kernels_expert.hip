@@ -37,20 +37,26 @@
 namespace fp8moe {
 
 // ------------------------------------------------------------------ grouped GEMM
+// W compute waves + 1 loader wave, W = blockDim.x/64 - 1 in [1, 8].  Up to
+// five compute waves two workgroups share a CU; more make one workgroup per
+// CU whose activation chunks serve more weight rows.
 template <int MSUB, int NB, bool GATEUP>
-__global__ __launch_bounds__(320, 3) void wsgemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kGemmMaxThreads) void wsgemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t abuf[kGemmLdsBytes];
   wsgemm_tile<MSUB, NB, GATEUP>(g, blockIdx.x, abuf);
 }
 
 // ------------------------------------------------------------------ down, fp32 products
 // No-requant mode: y[row][c] = (sum_o h[row][o] dec(Wd[c][o])) * s_down[c] on
-// v_mfma_f32_16x16x4_f32.  Instruction i of a 128-wide K step takes K index
-// 32*(l/16) + i from lane l, for A and B alike.  An accuracy mode: simple
+// v_mfma_f32_16x16x4_f32.  Lane l (channel l%16, group kg = l/16) owns, of
+// each 128-wide K step, the indices [16kg, +16) and [64 + 16kg, +16) -- the
+// two 16-byte pieces of its weight tile -- and instruction q of the step
+// takes the q-th of them, for A and B alike.  An accuracy mode: simple
 // direct loads, no prefetch pipeline.
 __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
   const RowSpace &rs = g.rs;
   const int d = rs.d, f = rs.f;
+  const int KT = (f + 127) >> 7;
   const int n_tiles = (d + 63) >> 6;
   const int item_id = blockIdx.x / n_tiles;
   const int tile = blockIdx.x - item_id * n_tiles;
@@ -58,33 +64,29 @@ __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
   if (!resolve_item(rs, item_id, expert, row0, rows)) return;
   const bool shared = expert >= rs.E;
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
-  const uint8_t *wd = (shared ? g.w.ws_down : g.w.w_down) + ex * d * f;
+  const uint8_t *wd = (shared ? g.w.ws_down : g.w.w_down) + ex * d * (size_t)KT * 128;
   const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * d;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ln = lane & 15, kg = lane >> 4;
   const int oc = (tile << 6) + (wave << 4) + ln;
-  const uint8_t *bp = wd + (size_t)(oc < d ? oc : d - 1) * f + kg * 32;
-  const int nk = (f + 127) >> 7;
+  const uint8_t *bp = wd + (size_t)((oc < d ? oc : d - 1) >> 4) * KT * 2048 + lane * 16;
   const bool half_tail = (f & 127) != 0;
   for (int r0 = 0; r0 < rows; r0 += 16) {
     const int r = r0 + ln;
     const bool aok = r < rows && row_real(rs, row0 + r);
-    const float *arow = g.a32 + (size_t)(row0 + (r < rows ? r : 0)) * f + kg * 32;
+    const float *arow = g.a32 + (size_t)(row0 + (r < rows ? r : 0)) * f + kg * 16;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < nk; ++ks) {
-      const int k = ks << 7;
-      const bool kval = !(half_tail && ks == nk - 1 && kg >= 2);
-      v4i w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
-      if (kval) {
-        w0 = load16(bp + k);
-        w1 = load16(bp + k + 16);
-      }
+    for (int ks = 0; ks < KT; ++ks) {
+      const bool hi_ok = !(half_tail && ks == KT - 1);  // K past f: zero weights, no A read
+      const v4i w0 = load16(bp + ks * 2048);
+      const v4i w1 = load16(bp + ks * 2048 + 1024);
       const uint32_t ww[8] = {(uint32_t)w0.x, (uint32_t)w0.y, (uint32_t)w0.z, (uint32_t)w0.w,
                               (uint32_t)w1.x, (uint32_t)w1.y, (uint32_t)w1.z, (uint32_t)w1.w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         v4f av = {0.f, 0.f, 0.f, 0.f};
-        if (aok && kval) av = *reinterpret_cast<const v4f *>(arow + k + 4 * q);
+        if (aok && (q < 4 || hi_ok))
+          av = *reinterpret_cast<const v4f *>(arow + ks * 128 + (q < 4 ? 4 * q : 64 + 4 * (q - 4)));
         const v2f lo = e4m3x2_to_f32<false>(ww[q]);
         const v2f hi = e4m3x2_to_f32<true>(ww[q]);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, lo.x, acc, 0, 0, 0);
@@ -102,6 +104,33 @@ __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ weight tile order
+// Thread q writes bytes [16q, +16) of the tile-order matrix (moe_weights):
+// tile q/128, half (q%128)/64, lane l = q%64 -> row 16*(tile/CT) + l%16,
+// columns 128*(tile%CT) + 64*half + 16*(l/16) + [0, 16), zero past cols.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t *__restrict__ codes,
+                                                           int rows, int cols,
+                                                           uint8_t *__restrict__ packed) {
+  const int CT = (cols + 127) >> 7;
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (size_t)rows * CT * 8) return;
+  const size_t tile = q >> 7;
+  const int piece = (int)(q & 127), half = piece >> 6, l = piece & 63;
+  const int r = (int)(tile / CT) * 16 + (l & 15);
+  const int c = (int)(tile % CT) * 128 + half * 64 + (l >> 4) * 16;
+  v4i v = {0, 0, 0, 0};
+  if (c < cols) v = load16(codes + (size_t)r * cols + c);
+  *reinterpret_cast<v4i *>(packed + q * 16) = v;
+}
+
+hipError_t launch_pack_weights(const uint8_t *codes, int32_t rows, int32_t cols, uint8_t *packed,
+                               hipStream_t stream) {
+  const size_t n = (size_t)rows * ((cols + 127) / 128) * 8;
+  if (n == 0) return hipSuccess;
+  pack_weights_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(codes, rows, cols, packed);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ requant
@@ -128,10 +157,14 @@ __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *
 static int grid_items(const RowSpace &rs) { return rs.items ? rs.max_items : rs.E + rs.S; }
 
 template <int MSUB, int NB, bool GATEUP>
-static hipError_t launch_ws(const GemmArgs &g, int n_tiles, hipStream_t stream) {
+static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
+  const int N = GATEUP ? g.rs.f : g.rs.d;
+  const int ch_wave = GATEUP ? 16 : 16 * NB;
+  const int wv = waves < 1 ? 1 : waves > kGemmMaxWaves ? kGemmMaxWaves : waves;
+  const int n_tiles = (N + wv * ch_wave - 1) / (wv * ch_wave);
   const int blocks = grid_items(g.rs) * n_tiles * g.splits;
   if (blocks == 0) return hipSuccess;
-  wsgemm_kernel<MSUB, NB, GATEUP><<<blocks, 320, 0, stream>>>(g);
+  wsgemm_kernel<MSUB, NB, GATEUP><<<blocks, (wv + 1) * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 
@@ -139,13 +172,13 @@ static hipError_t launch_ws(const GemmArgs &g, int n_tiles, hipStream_t stream) 
 int32_t chunk_bytes(int32_t msub) { return 128 * (8 / msub); }
 
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
-                          const ExpertWeights &w, float *h, int32_t msub, hipStream_t stream) {
+                          const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
+                          hipStream_t stream) {
   GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
-  const int n_tiles = rs.f / 64;
-  if (msub >= 8) return launch_ws<8, 2, true>(g, n_tiles, stream);
-  if (msub >= 4) return launch_ws<4, 2, true>(g, n_tiles, stream);
-  if (msub >= 2) return launch_ws<2, 2, true>(g, n_tiles, stream);
-  return launch_ws<1, 2, true>(g, n_tiles, stream);
+  if (msub >= 8) return launch_ws<8, 2, true>(g, waves, stream);
+  if (msub >= 4) return launch_ws<4, 2, true>(g, waves, stream);
+  if (msub >= 2) return launch_ws<2, 2, true>(g, waves, stream);
+  return launch_ws<1, 2, true>(g, waves, stream);
 }
 
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
@@ -173,7 +206,7 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
 
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
-                       hipStream_t stream) {
+                       int32_t waves, hipStream_t stream) {
   if (h32) {
     GemmArgs g{rs, nullptr, nullptr, h32, w, y, 1, rs.f};
     const int blocks = grid_items(rs) * ((rs.d + 63) >> 6);
@@ -184,13 +217,12 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   int32_t ksplit;
   down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
-  // 32 channels per wave, 128 per workgroup: the activation rows each
-  // workgroup loads are shared by twice the weight bytes.
-  const int n_tiles = (rs.d + kDownChannels - 1) / kDownChannels;
-  if (msub >= 8) return launch_ws<8, 2, false>(g, n_tiles, stream);
-  if (msub >= 4) return launch_ws<4, 2, false>(g, n_tiles, stream);
-  if (msub >= 2) return launch_ws<2, 2, false>(g, n_tiles, stream);
-  return launch_ws<1, 2, false>(g, n_tiles, stream);
+  // 32 channels per wave: the activation rows each workgroup loads are
+  // shared by twice the weight bytes.
+  if (msub >= 8) return launch_ws<8, 2, false>(g, waves, stream);
+  if (msub >= 4) return launch_ws<4, 2, false>(g, waves, stream);
+  if (msub >= 2) return launch_ws<2, 2, false>(g, waves, stream);
+  return launch_ws<1, 2, false>(g, waves, stream);
 }
 
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,

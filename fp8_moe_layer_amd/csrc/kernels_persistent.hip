@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kPThreads, 3) void moe_persistent_kernel(PersistArg
   // ---- 6. down grouped GEMM (K splits into separate slabs)
   {
     const GemmArgs g{rs, a.hq, a.sh, nullptr, a.w, a.y, a.splits, a.ksplit};
-    const int n = rs.max_items * ((d + kDownChannels - 1) / kDownChannels) * a.splits;
+    const int n = rs.max_items * ((d + 4 * kDownChannelsPerWave - 1) / (4 * kDownChannelsPerWave)) * a.splits;
     for (int b = B; b < n; b += G) wsgemm_tile<MSUB, 2, false>(g, b, lds);
   }
   grid_barrier();

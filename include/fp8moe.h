@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FP8MOE_ABI_VERSION 1
+#define FP8MOE_ABI_VERSION 2
 
 typedef int32_t moe_status;
 enum {
@@ -93,11 +93,23 @@ typedef struct {
   uint32_t flags;   /* MOE_F_* */
 } moe_dims;
 
-/* Expert weights: e4m3 codes (one byte each) and fp32 per-output-channel scales. */
+/* Expert weights: e4m3 codes (one byte each) in MFMA tile order, and fp32
+ * per-output-channel scales.
+ *
+ * Tile order of a code matrix W [R][C] (R output channels, a multiple of 16;
+ * C inputs, a multiple of 64), as written by moe_pack_weights: with
+ * CT = ceil(C / 128), 2048-byte tiles indexed by (r / 16) * CT + c / 128, and
+ * inside a tile, for l = (r % 16) + 16 * ((c % 64) / 16):
+ *   W[r][c] at byte  l * 16 + c % 16          when c % 128 <  64,
+ *              byte  1024 + l * 16 + c % 16   when c % 128 >= 64;
+ * bytes for c >= C are zero.  A tile is the weight operand of one
+ * v_mfma_f32_16x16x128_f8f6f4 (lane l reads 16 contiguous bytes from each
+ * half), so a wave loads it as two fully contiguous 1 KB pieces.
+ * Size of one matrix: moe_packed_weight_bytes(R, C) = R * CT * 128. */
 typedef struct {
-  const uint8_t *w_gate, *w_up; /* [E][f][d] row-major (d contiguous) */
+  const uint8_t *w_gate, *w_up; /* [E] tile-order matrices of [f][d] */
   const float *s_gate, *s_up;   /* [E][f] */
-  const uint8_t *w_down;        /* [E][d][f] row-major (f contiguous) */
+  const uint8_t *w_down;        /* [E] tile-order matrices of [d][f] */
   const float *s_down;          /* [E][d] */
   const uint8_t *ws_gate, *ws_up, *ws_down; /* shared experts: same layouts with */
   const float *ss_gate, *ss_up, *ss_down;   /* n_shared in place of E; NULL when 0 */
@@ -114,6 +126,18 @@ typedef struct {
  * cols: multiple of 4; x 16-byte aligned; q 4-byte aligned. */
 moe_status moe_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t *q, float *scale,
                              void *stream);
+
+/* Bytes of one weight matrix of R output channels by C inputs in tile order
+ * (see moe_weights); 0 when R is not a positive multiple of 16 or C not a
+ * positive multiple of 64. */
+int64_t moe_packed_weight_bytes(int32_t rows, int32_t cols);
+
+/* Reorders row-major e4m3 codes [rows][cols] into tile order (moe_weights)
+ * at packed (moe_packed_weight_bytes(rows, cols) bytes, zero padding
+ * included).  rows multiple of 16, cols multiple of 64 up to 16384; codes
+ * and packed 16-byte aligned and not overlapping. */
+moe_status moe_pack_weights(const uint8_t *codes, int32_t rows, int32_t cols, uint8_t *packed,
+                            void *stream);
 
 /* Router scores ("Routage MoE entre GPU", the router paragraph):
  * logits[t][e] = sum_i x[t][i] * w_router[e][i] (+ bias[e]), fp32.
@@ -154,7 +178,8 @@ moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_
 /* "Expert rows" layout used by the three expert stages below: rows
  * [0, capacity) follow sorted_pairs (padding rows hold garbage or zeros);
  * row capacity + s*T + t is token t for shared expert s.
- * rows_total = capacity + n_shared*T. */
+ * rows_total = capacity + n_shared*T.  w_gate[e][o][i] below is the logical
+ * element (row o, column i) of expert e's matrix, stored in tile order. */
 
 /* Gate/up grouped GEMM with the SwiGLU epilogue, for every expert row:
  *   g[o] = (sum_i dec(xq[t][i]) * dec(w_gate[e][o][i])) * sx[t] * s_gate[e][o]

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.ABI_VERSION == 1
+    assert fp8.ABI_VERSION == 2
     assert fp8._status_str(0) == b"ok"
     assert fp8._status_str(ERR_WORKSPACE) == b"workspace too small"
     assert fp8._status_str(99) == b"unknown status"
@@ -113,6 +113,19 @@ def test_fused_forward_rejects_null_and_alignment_and_workspace():
         pers.flags = fp8.MOE_F_PERSISTENT | extra
         assert call(dims=pers) == ERR_UNSUPPORTED
         assert b"switched off" in fp8._last_error()
+
+
+def test_packed_weight_bytes_and_pack_validation():
+    assert fp8.packed_weight_bytes(16, 64) == 16 * 128          # tail padded to a full tile
+    assert fp8.packed_weight_bytes(32, 256) == 32 * 256
+    assert fp8.packed_weight_bytes(4096, 14336) == 4096 * 14336
+    for r, c in ((0, 64), (8, 64), (16, 32), (16, 0), (-16, 64)):
+        assert fp8.packed_weight_bytes(r, c) == 0
+    assert fp8._pack_weights(None, 16, 64, FAKE, None) == ERR_NULL
+    assert fp8._pack_weights(FAKE, 24, 64, FAKE + (1 << 30), None) == ERR_SHAPE
+    assert fp8._pack_weights(FAKE, 16, 16384 + 64, FAKE + (1 << 30), None) == ERR_SHAPE
+    assert fp8._pack_weights(FAKE + 4, 16, 64, FAKE + (1 << 30), None) == ERR_ALIGN
+    assert fp8._pack_weights(FAKE, 16, 128, FAKE + 1024, None) == ERR_SHAPE  # overlap
 
 
 def test_step_entry_points_reject_bad_arguments():

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import workloads as wl
+import tile_layout as tl
 from gpu_common import Layer, dev, lib, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu,
@@ -97,7 +98,9 @@ def test_equal_logits_tie_stress(small):
 
 
 def test_weights_match_oracle_quantiser(small):
-    np.testing.assert_array_equal(to_np(small.dw.w_gate), small.qw.w_gate)
+    sp = small.spec
+    np.testing.assert_array_equal(tl.unpack(to_np(small.dw.w_gate), sp.f, sp.d), small.qw.w_gate)
+    np.testing.assert_array_equal(tl.unpack(to_np(small.dw.w_down), sp.d, sp.f), small.qw.w_down)
     np.testing.assert_array_equal(to_np(small.dw.s_down), small.qw.s_down)
 
 

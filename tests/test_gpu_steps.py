@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import workloads as wl
+import tile_layout as tl
 from gpu_common import Layer, dev, lib, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu,
@@ -142,6 +143,29 @@ def test_permute_bit_exact(T, E, k, bm, var):
         np.testing.assert_array_equal(to_np(p[key]), po[key], err_msg=key)
 
 
+# ----------------------------------------------------------------- weight tile order
+
+@pytest.mark.parametrize("R,C", [(16, 64), (48, 192), (64, 4096), (1408, 2048), (4096, 14336),
+                                 (32, 16384)])
+def test_pack_weights_bit_exact(R, C):
+    """moe_pack_weights against the layout's definition (tests/tile_layout),
+    including the zero padding of a 64-wide tail."""
+    m = lib()
+    rng = np.random.default_rng(R + C)
+    codes = rng.integers(0, 256, (R, C), dtype=np.uint8)
+    packed = m.pack_weights(torch.from_numpy(codes).to(dev()))
+    assert packed.numel() == m.packed_weight_bytes(R, C)
+    np.testing.assert_array_equal(to_np(packed), tl.pack(codes))
+
+
+def test_pack_weights_rejects_bad_shapes():
+    m = lib()
+    codes = torch.zeros((24, 64), dtype=torch.uint8, device=dev())
+    with pytest.raises(m.MoEError):
+        m.pack_weights(codes, torch.empty(24 * 128, dtype=torch.uint8, device=dev()))
+    assert m.packed_weight_bytes(24, 64) == 0 and m.packed_weight_bytes(16, 96) == 0
+
+
 # ----------------------------------------------------------------- expert products
 
 def _planted(rng, rows, cols, at, zero):
@@ -177,7 +201,8 @@ def test_expert_products_integer_exact(T, d, f, E, k, S):
         dw.set_expert("gate", i, torch.from_numpy(wg[e]).to(dev()), sh)
         dw.set_expert("up", i, torch.from_numpy(wu[e]).to(dev()), sh)
         dw.set_expert("down", i, torch.from_numpy(wd[e]).to(dev()), sh)
-    np.testing.assert_array_equal(to_np(dw.w_gate), qw.w_gate)
+    np.testing.assert_array_equal(tl.unpack(to_np(dw.w_gate), f, d), qw.w_gate)
+    np.testing.assert_array_equal(tl.unpack(to_np(dw.w_down), d, f), qw.w_down)
     ids, _ = oracle.route_topk(rng.standard_normal((T, E)).astype(np.float32), k)
     bm = 16
     perm_o = oracle.permute(ids, E, bm)
