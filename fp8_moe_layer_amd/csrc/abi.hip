@@ -8,6 +8,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/fp8moe.h"
 #include "internal.hpp"
 
@@ -103,11 +105,11 @@ int env_int(const char *name, int dflt) {
 int32_t choose_msub(const moe_dims *d) {
   // tile-tuning override (power of two, 1..8)
   const int forced = env_int("FP8MOE_MSUB", 0);
-  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
+  if (forced == 1 || forced == 2 || forced == 4 || forced == 8 || forced == 16) return forced;
   const double mean = (double)d->T * d->k_max / d->E;
   const double est = mean + 4.0 * sqrt(mean) + 2.0;
   int32_t m = 1;
-  while (m < 8 && 16.0 * m < est) m <<= 1;
+  while (m < 16 && 16.0 * m < est) m <<= 1;
   return m;
 }
 
@@ -120,18 +122,23 @@ double expected_active(const moe_dims *d) {
 // Expected work items of the grouped GEMMs (rows cut into 16*msub chunks).
 double expected_items(const moe_dims *d, int32_t msub) {
   const double chunk = 16.0 * msub;
-  const double rows = (double)d->T * d->k_max / d->E + d->block_m - 1;
+  const double mean = (double)d->T * d->k_max / d->E;
+  const double rows = ceil(mean / d->block_m) * d->block_m;  // padded segment
   const double per = rows > chunk ? ceil(rows / chunk) : 1.0;
   return expected_active(d) * per + d->n_shared * ceil(d->T / chunk);
 }
 
 // Grouped-GEMM geometry.  A workgroup of W compute waves covers
-// W * ch_wave output channels; up to five compute waves two workgroups
-// share a CU, more make one per CU.  The work is a whole number of rounds
-// of resident workgroups, so W is chosen to waste least of the last round
-// and of partial channel tiles: efficiency = (workgroups / (rounds * slots))
-// * (N / (tiles * W * ch_wave)), ties to the larger W (fewer activation
-// re-reads).  K splits (down only) aim at two rounds.
+// W * ch_wave output channels of one work item (and one K split).  Up to
+// five compute waves (row passes of up to 128 rows) two workgroups share a
+// CU, otherwise one.  A simple model picks W and the K splits: workgroups
+// run in whole rounds of resident ones; a CU streams weights at a rate that
+// grows with its resident compute waves up to about six; a workgroup's
+// time is proportional to its weight bytes; each K split adds one fp32
+// slab of y to write and to read back.  The estimated time per CU is
+//   rounds * wg_per_cu * W*ch_wave*K/splits / min(1, waves_per_cu/6)
+//   + splits * 2 * rows * N * 4 / CUs,
+// minimised with ties going to the larger W and the fewer splits.
 struct GemmPlan {
   int32_t waves, splits;
 };
@@ -141,29 +148,36 @@ constexpr int kCUs = 256;
 GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
   const double items = expected_items(d, msub);
   const int N = gate_up ? d->f : d->d;
+  const int K = gate_up ? d->d : d->f;
   const int ch_wave = gate_up ? 16 : kDownChannelsPerWave;
-  const int forced = env_int("FP8MOE_WAVES", 0);  // tile-tuning override
-  GemmPlan best{4, 1};
-  double best_eff = -1.0;
-  for (int W = kGemmMaxWaves; W >= 3; --W) {
-    if (forced >= 1 && forced <= kGemmMaxWaves && W != forced) continue;
-    const double slots = (double)kCUs * (W <= 5 ? 2 : 1);
+  const double rows = (double)d->T * d->k_max + (double)d->n_shared * d->T;
+  const int forced = env_int("FP8MOE_WAVES", 0);            // tile-tuning overrides
+  const int forced_splits = env_int("FP8MOE_DOWN_SPLITS", 0);
+  const bool can_split = !gate_up && !(d->flags & MOE_F_NO_REQUANT);
+  const int maxw = msub > 8 ? kGemmMaxWaves16 : kGemmMaxWaves;
+  GemmPlan best{maxw, 1};
+  double best_t = 1e300;
+  for (int W = maxw; W >= 1; --W) {
+    if (forced >= 1 && forced <= maxw && W != forced) continue;
+    const int per_cu = (W <= 5 && msub <= 8) ? 2 : 1;
+    const double slots = (double)kCUs * per_cu;
     const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);
-    int32_t splits = 1;
-    if (!gate_up && !(d->flags & MOE_F_NO_REQUANT)) {
-      const int want = (int)ceil(2.0 * slots / (items * tiles));
-      splits = down_splits_used(d->f, msub, want < 1 ? 1 : want > 8 ? 8 : want);
-    }
-    const double n = items * tiles * splits;
-    const double rounds = ceil(n / slots);
-    const double eff = (n / (rounds * slots)) * ((double)N / ((double)tiles * W * ch_wave));
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = GemmPlan{W, splits};
+    const double rate = std::min(1.0, W * per_cu / 6.0);
+    int last = 0;
+    for (int want = 1; want <= (can_split ? 8 : 1); ++want) {
+      const int sp = can_split ? down_splits_used(d->f, msub, forced_splits > 0 ? forced_splits : want) : 1;
+      if (sp == last) continue;
+      last = sp;
+      const double n = items * tiles * sp;
+      const double rounds = ceil(n / slots);
+      const double t = rounds * per_cu * (double)W * ch_wave * K / sp / rate +
+                       sp * 2.0 * rows * N * 4.0 / kCUs;
+      if (t < best_t * (1.0 - 1e-9)) {
+        best_t = t;
+        best = GemmPlan{W, sp};
+      }
     }
   }
-  const int fs = env_int("FP8MOE_DOWN_SPLITS", 0);  // tile-tuning override
-  if (!gate_up && fs > 0 && !(d->flags & MOE_F_NO_REQUANT)) best.splits = down_splits_used(d->f, msub, fs);
   return best;
 }
 

@@ -101,23 +101,31 @@ static __device__ __attribute__((aligned(64))) uint8_t g_zero_piece[64];
 
 template <int MSUB>
 struct Chunk {
-  static constexpr int MP = 16 * MSUB;           // rows per pass
-  static constexpr int KSC = 8 / MSUB;           // K steps per chunk: 16 KB of activations
-  static constexpr int BYTES = MSUB * KSC * 2048;
-  static constexpr int NBUF = 4;                 // LDS ring; the loader runs NBUF-1 chunks ahead
-  static constexpr int LPC = MSUB * KSC * 2;     // direct-to-LDS loads per chunk (always 16)
+  static constexpr int MP = 16 * MSUB;                 // rows per pass
+  static constexpr int KSC = MSUB >= 8 ? 1 : 8 / MSUB; // K steps per chunk
+  static constexpr int BYTES = MSUB * KSC * 2048;      // 16 KB (32 KB for 256-row passes)
+  static constexpr int NBUF = 4;                       // LDS ring; loads run NBUF-1 chunks ahead
+  static constexpr int LOADERS = MSUB > 8 ? 2 : 1;     // loader waves, 16 loads per chunk each
+  static constexpr int LPC = MSUB * KSC * 2 / LOADERS; // direct-to-LDS loads per chunk and loader
+  static constexpr int MPL = MSUB / LOADERS;           // row groups per loader wave
   // weight prefetch depth in k steps (registers allow 4 when few row tiles)
   static constexpr int PF = MSUB <= 2 ? 4 : 2;
+  // LDS: the activation ring, then a table of the activation scale of each
+  // row of the current pass (two copies by pass parity), 0 for a padding
+  // row.  The loader waves fill the table with the same row lookups they
+  // make for the gather, so the epilogue needs no global loads on its
+  // critical path.
+  static constexpr int RING = NBUF * BYTES;
+  static constexpr int LDS = RING + 2 * MP * (int)sizeof(float);
 };
 
-// LDS of a grouped-GEMM workgroup: the activation ring, then a table of the
-// activation scale of each row of the current row pass (two copies by pass
-// parity), 0 for a padding row.  The loader wave fills the table with the
-// same row lookups it makes for the gather, so the epilogue needs no global
-// loads on its critical path.
-constexpr int kGemmRingBytes = Chunk<1>::NBUF * Chunk<1>::BYTES;
-constexpr int kGemmRowTable = 2 * 16 * 8;  // floats: two passes of up to 128 rows
-constexpr int kGemmLdsBytes = kGemmRingBytes + kGemmRowTable * (int)sizeof(float);
+// LDS of the persistent kernel's GEMM phases (row passes of up to 128 rows).
+constexpr int kGemmLdsBytes = Chunk<8>::LDS;
+
+// K granule of a split: whole chunks.
+__host__ __device__ constexpr int split_granule(int msub) {
+  return 128 * (msub >= 8 ? 1 : 8 / msub);
+}
 
 // s_waitcnt vmcnt(n * 16): n chunks of loads may stay in flight.
 __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
@@ -132,15 +140,15 @@ __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
 // GATEUP: out = h[rows][f], NB must be 2 (gate row, up row of the same channel).
 // else:   out = y[split][rows][d], NB channel groups of 16 per wave.
 // One call computes tile `bid` (= (item * n_tiles + tile) * splits + split)
-// with a workgroup of W = blockDim.x/64 - 1 compute waves (1..8) and one
-// loader wave (wave W); the tile is W * 16 * (GATEUP ? 1 : NB) output
-// channels wide.  abuf: kGemmLdsBytes of LDS, 1024-byte aligned.  Returns
+// with a workgroup of W = blockDim.x/64 - LOADERS compute waves followed by
+// the loader wave(s); the tile is W * 16 * (GATEUP ? 1 : NB) output channels
+// wide.  abuf: Chunk<MSUB>::LDS bytes of LDS, 1024-byte aligned.  Returns
 // early (uniformly) for an empty item.
 template <int MSUB, int NB, bool GATEUP>
 __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t *abuf) {
-  const int W = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6) - 1);  // compute waves
   using C = Chunk<MSUB>;
   static_assert(C::LPC == 16 && C::NBUF == 4, "loader_wait_barrier assumes 16 loads per chunk");
+  const int W = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6) - C::LOADERS);  // compute waves
 
   const RowSpace &rs = g.rs;
   const int K = GATEUP ? rs.d : rs.f;
@@ -170,18 +178,21 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kg = lane >> 4;
 
-  float *row_scale = reinterpret_cast<float *>(abuf + kGemmRingBytes);
+  float *row_scale = reinterpret_cast<float *>(abuf + C::RING);
 
-  if (wave == W) {
-    // ---------------- loader wave: activation rows -> LDS, chunk by chunk
-    const uint8_t *abase[MSUB];
+  if (wave >= W) {
+    // ---------------- loader waves: activation rows -> LDS, chunk by chunk;
+    // loader j gathers row groups [j*MPL, (j+1)*MPL)
+    const int mbase = (wave - W) * C::MPL;
+    const uint8_t *abase[C::MPL];
     int pass = 0;
     for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
       const int prow = min(C::MP, rows - p0);
       const int msub = (prow + 15) >> 4;
-      float *rsc = row_scale + (pass & 1) * 128;
+      float *rsc = row_scale + (pass & 1) * C::MP;
 #pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
+      for (int mm = 0; mm < C::MPL; ++mm) {
+        const int m = mbase + mm;
         const int r = p0 + m * 16 + ln;
         const uint8_t *b = nullptr;
         float sc = 0.0f;
@@ -197,7 +208,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
             sc = g.a_scale[row0 + r];
           }
         }
-        abase[m] = b;
+        abase[mm] = b;
         if (kg == 0) rsc[m * 16 + ln] = sc;
       }
       // the table is complete before the first barrier of the pass
@@ -205,13 +216,14 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
       auto issue = [&](int c) {
         uint8_t *dst = abuf + (c % C::NBUF) * C::BYTES;
 #pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
+        for (int mm = 0; mm < C::MPL; ++mm) {
+          const int m = mbase + mm;
 #pragma unroll
           for (int s = 0; s < C::KSC; ++s) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
               const int kb = k_begin + (c * C::KSC + s) * 128 + p * 64 + kg * 16;
-              const uint8_t *src = (abase[m] && kb < k_end) ? abase[m] + kb : g_zero_piece;
+              const uint8_t *src = (abase[mm] && kb < k_end) ? abase[mm] + kb : g_zero_piece;
               __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ((m * C::KSC + s) * 2 + p) * 1024),
                                                16, 0, 0);
             }
@@ -273,7 +285,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
     const int prow = min(C::MP, rows - p0);
     const int msub = (prow + 15) >> 4;
-    const float *rsc = row_scale + (pass & 1) * 128;
+    const float *rsc = row_scale + (pass & 1) * C::MP;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll

@@ -64,6 +64,9 @@ int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int
 // five, two workgroups share a CU).
 constexpr int kGemmMaxWaves = 8;
 constexpr int kGemmMaxThreads = (kGemmMaxWaves + 1) * 64;
+// 256-row passes (msub 16): two loader waves, at most six compute waves.
+constexpr int kGemmMaxWaves16 = 6;
+constexpr int kGemmMaxThreads16 = (kGemmMaxWaves16 + 2) * 64;
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
                           hipStream_t stream);
@@ -78,8 +81,6 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
                        int32_t waves, hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
-// K bytes per LDS chunk of the grouped GEMMs for a row-pass size.
-int32_t chunk_bytes(int32_t msub);
 // Final K-split count and bytes per split for a requested split count.
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
                          int32_t *ksplit);

@@ -37,12 +37,13 @@
 namespace fp8moe {
 
 // ------------------------------------------------------------------ grouped GEMM
-// W compute waves + 1 loader wave, W = blockDim.x/64 - 1 in [1, 8].  Up to
-// five compute waves two workgroups share a CU; more make one workgroup per
-// CU whose activation chunks serve more weight rows.
+// W compute waves + the loader wave(s).  With up to five compute waves and
+// row passes of up to 128 rows two workgroups share a CU; otherwise one
+// workgroup per CU (256-row passes use 130 KB of LDS and up to 256 VGPRs).
 template <int MSUB, int NB, bool GATEUP>
-__global__ __launch_bounds__(kGemmMaxThreads) void wsgemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t abuf[kGemmLdsBytes];
+__global__ __launch_bounds__(MSUB > 8 ? kGemmMaxThreads16 : kGemmMaxThreads) void wsgemm_kernel(
+    GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[Chunk<MSUB>::LDS];
   wsgemm_tile<MSUB, NB, GATEUP>(g, blockIdx.x, abuf);
 }
 
@@ -160,21 +161,21 @@ template <int MSUB, int NB, bool GATEUP>
 static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
   const int N = GATEUP ? g.rs.f : g.rs.d;
   const int ch_wave = GATEUP ? 16 : 16 * NB;
-  const int wv = waves < 1 ? 1 : waves > kGemmMaxWaves ? kGemmMaxWaves : waves;
+  const int maxw = MSUB > 8 ? kGemmMaxWaves16 : kGemmMaxWaves;
+  const int wv = waves < 1 ? 1 : waves > maxw ? maxw : waves;
   const int n_tiles = (N + wv * ch_wave - 1) / (wv * ch_wave);
   const int blocks = grid_items(g.rs) * n_tiles * g.splits;
   if (blocks == 0) return hipSuccess;
-  wsgemm_kernel<MSUB, NB, GATEUP><<<blocks, (wv + 1) * 64, 0, stream>>>(g);
+  wsgemm_kernel<MSUB, NB, GATEUP><<<blocks, (wv + Chunk<MSUB>::LOADERS) * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 
-// K bytes per LDS chunk for a row-pass size (the K-split granularity).
-int32_t chunk_bytes(int32_t msub) { return 128 * (8 / msub); }
 
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
                           hipStream_t stream) {
   GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
+  if (msub >= 16) return launch_ws<16, 2, true>(g, waves, stream);
   if (msub >= 8) return launch_ws<8, 2, true>(g, waves, stream);
   if (msub >= 4) return launch_ws<4, 2, true>(g, waves, stream);
   if (msub >= 2) return launch_ws<2, 2, true>(g, waves, stream);
@@ -191,7 +192,7 @@ hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float
 
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
                          int32_t *ksplit) {
-  const int kc = chunk_bytes(msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
+  const int kc = split_granule(msub >= 16 ? 16 : msub >= 8 ? 8 : msub >= 4 ? 4 : msub >= 2 ? 2 : 1);
   const int nchunks = (f + kc - 1) / kc;
   const int s = requested < 1 ? 1 : (requested > nchunks ? nchunks : requested);
   *ksplit = ((nchunks + s - 1) / s) * kc;
@@ -219,6 +220,7 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
   // 32 channels per wave: the activation rows each workgroup loads are
   // shared by twice the weight bytes.
+  if (msub >= 16) return launch_ws<16, 2, false>(g, waves, stream);
   if (msub >= 8) return launch_ws<8, 2, false>(g, waves, stream);
   if (msub >= 4) return launch_ws<4, 2, false>(g, waves, stream);
   if (msub >= 2) return launch_ws<2, 2, false>(g, waves, stream);

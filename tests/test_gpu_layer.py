@@ -140,6 +140,16 @@ def test_persistent_single_launch_matches_staged(small):
     assert torch.equal(a, b) and torch.equal(b, b2)
 
 
+@pytest.mark.parametrize("msub,waves", [(16, 6), (16, 3), (8, 8), (8, 7), (2, 5), (1, 1)])
+def test_gemm_geometry_overrides(small, msub, waves, monkeypatch):
+    """Every row-pass height and compute-wave count of the grouped GEMMs
+    (tile-tuning overrides) gives the same parity, on every token."""
+    monkeypatch.setenv("FP8MOE_MSUB", str(msub))
+    monkeypatch.setenv("FP8MOE_WAVES", str(waves))
+    _check(small)
+    _check(small, no_requant=True)
+
+
 def test_persistent_flag_is_refused(small):
     for nr in (False, True):
         with pytest.raises(lib().MoEError):
