@@ -128,19 +128,21 @@ double expected_items(const moe_dims *d, int32_t msub) {
   return expected_active(d) * per + d->n_shared * ceil(d->T / chunk);
 }
 
-// Grouped-GEMM geometry.  A workgroup of W compute waves covers
-// W * ch_wave output channels of one work item (and one K split).  Up to
-// five compute waves (row passes of up to 128 rows) two workgroups share a
-// CU, otherwise one.  A simple model picks W and the K splits: workgroups
-// run in whole rounds of resident ones; a CU streams weights at a rate that
-// grows with its resident compute waves up to about six; a workgroup's
-// time is proportional to its weight bytes; each K split adds one fp32
-// slab of y to write and to read back.  The estimated time per CU is
-//   rounds * wg_per_cu * W*ch_wave*K/splits / min(1, waves_per_cu/6)
+// Grouped-GEMM geometry.  A workgroup of W compute waves, each holding nb
+// weight operands of 16 rows (2 or 4), covers W * ch_wave output channels
+// of one work item and one K split.  With nb 2, up to five compute waves
+// and row passes of up to 128 rows, two workgroups share a CU, otherwise
+// one.  A simple model picks (W, nb, splits): workgroups run in whole rounds
+// of resident ones; a CU streams weights at a rate that grows with the
+// weight loads it keeps in flight (resident waves * nb) up to about six
+// two-operand waves; a workgroup's time is proportional to its weight
+// bytes; each K split adds one fp32 slab of y to write and to read back.
+// The estimated time per CU,
+//   rounds * wg_per_cu * W*ch_wave*K/splits / min(1, waves_per_cu*nb/12)
 //   + splits * 2 * rows * N * 4 / CUs,
-// minimised with ties going to the larger W and the fewer splits.
+// is minimised, ties going to the larger W and the fewer splits.
 struct GemmPlan {
-  int32_t waves, splits;
+  int32_t waves, splits, nb;
 };
 
 constexpr int kCUs = 256;
@@ -149,32 +151,39 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
   const double items = expected_items(d, msub);
   const int N = gate_up ? d->f : d->d;
   const int K = gate_up ? d->d : d->f;
-  const int ch_wave = gate_up ? 16 : kDownChannelsPerWave;
   const double rows = (double)d->T * d->k_max + (double)d->n_shared * d->T;
   const int forced = env_int("FP8MOE_WAVES", 0);            // tile-tuning overrides
+  const int forced_nb = env_int("FP8MOE_NB", 0);
   const int forced_splits = env_int("FP8MOE_DOWN_SPLITS", 0);
   const bool can_split = !gate_up && !(d->flags & MOE_F_NO_REQUANT);
-  const int maxw = msub > 8 ? kGemmMaxWaves16 : kGemmMaxWaves;
-  GemmPlan best{maxw, 1};
+  GemmPlan best{4, 1, 2};
   double best_t = 1e300;
-  for (int W = maxw; W >= 1; --W) {
-    if (forced >= 1 && forced <= maxw && W != forced) continue;
-    const int per_cu = (W <= 5 && msub <= 8) ? 2 : 1;
-    const double slots = (double)kCUs * per_cu;
-    const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);
-    const double rate = std::min(1.0, W * per_cu / 6.0);
-    int last = 0;
-    for (int want = 1; want <= (can_split ? 8 : 1); ++want) {
-      const int sp = can_split ? down_splits_used(d->f, msub, forced_splits > 0 ? forced_splits : want) : 1;
-      if (sp == last) continue;
-      last = sp;
-      const double n = items * tiles * sp;
-      const double rounds = ceil(n / slots);
-      const double t = rounds * per_cu * (double)W * ch_wave * K / sp / rate +
-                       sp * 2.0 * rows * N * 4.0 / kCUs;
-      if (t < best_t * (1.0 - 1e-9)) {
-        best_t = t;
-        best = GemmPlan{W, sp};
+  // four operands per wave measured no faster than two on this chip's
+  // decode and prefill shapes; they stay a tile-tuning option
+  const int nb_first = (forced_nb == 4 && msub <= 8) ? 4 : 2;
+  for (int nb = nb_first; nb >= 2; nb -= 2) {
+    const int ch_wave = gate_up ? 8 * nb : 16 * nb;
+    const int maxw = msub > 8 ? kGemmMaxWaves16 : nb > 2 ? kGemmMaxThreadsWide / 64 - 1 : kGemmMaxWaves;
+    for (int W = maxw; W >= 1; --W) {
+      if (forced >= 1 && forced <= maxw && W != forced) continue;
+      const int per_cu = (nb == 2 && W <= 5 && msub <= 8) ? 2 : 1;
+      const double slots = (double)kCUs * per_cu;
+      const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);
+      const double rate = std::min(1.0, W * per_cu * nb / 12.0);
+      int last = 0;
+      for (int want = 1; want <= (can_split ? 8 : 1); ++want) {
+        const int sp =
+            can_split ? down_splits_used(d->f, msub, forced_splits > 0 ? forced_splits : want) : 1;
+        if (sp == last) continue;
+        last = sp;
+        const double n = items * tiles * sp;
+        const double rounds = ceil(n / slots);
+        const double t = rounds * per_cu * (double)W * ch_wave * K / sp / rate +
+                         sp * 2.0 * rows * N * 4.0 / kCUs;
+        if (t < best_t * (1.0 - 1e-9)) {
+          best_t = t;
+          best = GemmPlan{W, sp, nb};
+        }
       }
     }
   }
@@ -185,7 +194,8 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
 struct Layout {
   size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
       hq, sh, y, total;
-  int32_t capacity, rows_total, max_items, row_chunk, msub, splits, waves_gu, waves_dn;
+  int32_t capacity, rows_total, max_items, row_chunk, msub, splits;
+  GemmPlan gu, dn;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -196,10 +206,9 @@ Layout layout_of(const moe_dims *d) {
   L.rows_total = L.capacity + d->n_shared * d->T;
   L.msub = choose_msub(d);
   L.row_chunk = 16 * L.msub;
-  L.waves_gu = plan_gemm(d, L.msub, true).waves;
-  const GemmPlan dn = plan_gemm(d, L.msub, false);
-  L.waves_dn = dn.waves;
-  L.splits = dn.splits;
+  L.gu = plan_gemm(d, L.msub, true);
+  L.dn = plan_gemm(d, L.msub, false);
+  L.splits = L.dn.splits;
   L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
   const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
   size_t o = 0;
@@ -385,8 +394,9 @@ moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint
   if (!aligned(xq, 16)) return fail(MOE_ERR_ALIGN, "%s: xq must be 16-byte aligned", fn);
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
   const int32_t msub = choose_msub(dims);
-  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub,
-                                plan_gemm(dims, msub, true).waves, as_stream(stream)),
+  const GemmPlan gp = plan_gemm(dims, msub, true);
+  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub, gp.waves, gp.nb,
+                                as_stream(stream)),
                  fn);
   return s ? s : ok();
 }
@@ -406,8 +416,9 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
     return fail(MOE_ERR_ALIGN, "%s: the activation rows must be 16-byte aligned", fn);
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
   const int32_t msub = choose_msub(dims);
+  const GemmPlan dp = plan_gemm(dims, msub, false);
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
-                             msub, 1, plan_gemm(dims, msub, false).waves, as_stream(stream)),
+                             msub, 1, dp.waves, dp.nb, as_stream(stream)),
                  fn);
   return s ? s : ok();
 }
@@ -486,18 +497,29 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
 
   mark(0);
   const float *lg = logits_override;
-  if (!lg) {
-    if ((s = hip_status(launch_route_logits(x, w_router, router_bias, dims->T, dims->d, dims->E,
-                                            logits, xq, sx, st),
-                        "router")))
+  if (!lg && route_fused_applies(dims->T, dims->E)) {
+    // one launch: logits, quantised x, top-k
+    if ((s = hip_status(launch_route_topk_fused(x, w_router, router_bias, dims->T, dims->d,
+                                                dims->E, dims->k_max, k_per_token, logits, xq, sx,
+                                                ids, tw, st),
+                        "route")))
       return s;
-    lg = logits;
-  } else if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) {
-    return s;
+    mark(1);
+  } else {
+    if (!lg) {
+      if ((s = hip_status(launch_route_logits(x, w_router, router_bias, dims->T, dims->d, dims->E,
+                                              logits, xq, sx, st),
+                          "router")))
+        return s;
+      lg = logits;
+    } else if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) {
+      return s;
+    }
+    mark(1);
+    if ((s = hip_status(launch_topk(lg, dims->T, dims->E, dims->k_max, k_per_token, ids, tw, st),
+                        "topk")))
+      return s;
   }
-  mark(1);
-  if ((s = hip_status(launch_topk(lg, dims->T, dims->E, dims->k_max, k_per_token, ids, tw, st), "topk")))
-    return s;
   mark(2);
   if ((s = hip_status(launch_permute(ids, dims->T, dims->E, dims->k_max, dims->block_m, L.capacity,
                                      sorted, offsets, block_expert, inv, n_blocks, items, n_items,
@@ -510,17 +532,17 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   rs.max_items = L.max_items;
   const ExpertWeights ew = to_internal(w);
   mark(3);
-  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.waves_gu, st), "gate_up"))) return s;
+  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.gu.waves, L.gu.nb, st), "gate_up"))) return s;
   mark(4);
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, L.waves_dn, st),
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, L.dn.waves, L.dn.nb, st),
                         "down")))
       return s;
   } else {
     mark(5);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, L.waves_dn, st), "down")))
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, L.dn.waves, L.dn.nb, st), "down")))
       return s;
   }
   mark(6);

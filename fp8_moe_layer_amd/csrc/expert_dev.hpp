@@ -137,11 +137,12 @@ __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// GATEUP: out = h[rows][f], NB must be 2 (gate row, up row of the same channel).
-// else:   out = y[split][rows][d], NB channel groups of 16 per wave.
+// GATEUP: out = h[rows][f]; a wave holds NB/2 channel groups of 16, each as
+//         a (gate rows, up rows) pair of weight operands.
+// else:   out = y[split][rows][d]; NB channel groups of 16 per wave.
 // One call computes tile `bid` (= (item * n_tiles + tile) * splits + split)
 // with a workgroup of W = blockDim.x/64 - LOADERS compute waves followed by
-// the loader wave(s); the tile is W * 16 * (GATEUP ? 1 : NB) output channels
+// the loader wave(s); the tile is W * (GATEUP ? 8 : 16) * NB output channels
 // wide.  abuf: Chunk<MSUB>::LDS bytes of LDS, 1024-byte aligned.  Returns
 // early (uniformly) for an empty item.
 template <int MSUB, int NB, bool GATEUP>
@@ -153,7 +154,8 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   const RowSpace &rs = g.rs;
   const int K = GATEUP ? rs.d : rs.f;
   const int N = GATEUP ? rs.f : rs.d;
-  constexpr int CH_WAVE = GATEUP ? 16 : 16 * NB;
+  static_assert(!GATEUP || NB % 2 == 0, "gate/up operands come in pairs");
+  constexpr int CH_WAVE = GATEUP ? 8 * NB : 16 * NB;
   const int CH_WG = W * CH_WAVE;
   const int n_tiles = (N + CH_WG - 1) / CH_WG;
   const int split = bid % g.splits;
@@ -251,8 +253,8 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
     int o;
     const uint8_t *wbase;
     if (GATEUP) {
-      o = tile * CH_WG + wave * 16 + ln;
-      wbase = (nb == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
+      o = tile * CH_WG + wave * CH_WAVE + (nb >> 1) * 16 + ln;
+      wbase = ((nb & 1) == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
               ex * (size_t)N * KT * 128;
     } else {
       o = tile * CH_WG + wave * CH_WAVE + nb * 16 + ln;
@@ -317,22 +319,25 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
 
     // ---------------- epilogue
     if (GATEUP) {
-      const int o = ch[0];
-      const bool live = o < N;  // a partial last tile computes a clamped row
-      const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + (live ? o : N - 1)];
-      const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + (live ? o : N - 1)];
 #pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        if (m < msub) {
+      for (int cg = 0; cg < NB / 2; ++cg) {
+        const int o = ch[2 * cg];
+        const bool live = o < N;  // a partial last tile computes a clamped row
+        const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + (live ? o : N - 1)];
+        const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + (live ? o : N - 1)];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = p0 + m * 16 + kg * 4 + i;
-            if (r < rows && live) {
-              // a padding row has scale 0 (and zero activations): h = 0
-              const float sxt = rsc[m * 16 + kg * 4 + i];
-              const float gv = acc[m][0][i] * sxt * sgo;
-              const float uv = acc[m][1][i] * sxt * suo;
-              g.out[(size_t)(row0 + r) * N + o] = gv / (1.0f + expf(-gv)) * uv;
+        for (int m = 0; m < MSUB; ++m) {
+          if (m < msub) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = p0 + m * 16 + kg * 4 + i;
+              if (r < rows && live) {
+                // a padding row has scale 0 (and zero activations): h = 0
+                const float sxt = rsc[m * 16 + kg * 4 + i];
+                const float gv = acc[m][2 * cg][i] * sxt * sgo;
+                const float uv = acc[m][2 * cg + 1][i] * sxt * suo;
+                g.out[(size_t)(row0 + r) * N + o] = gv / (1.0f + expf(-gv)) * uv;
+              }
             }
           }
         }
@@ -379,6 +384,38 @@ __device__ __forceinline__ void requant_row(const RowSpace &rs, const float *__r
                               red);
 }
 
+// One wave requantises one real expert row of up to 64*4*VEC values (the
+// row in registers); same arithmetic as requant_row.
+template <int VEC>
+__device__ __forceinline__ void requant_row_wave(const RowSpace &rs, const float *__restrict__ h,
+                                                 uint8_t *__restrict__ hq, float *__restrict__ sh,
+                                                 int row, int lane) {
+  if (!row_real(rs, row)) return;
+  const int f = rs.f;
+  const float *x = h + (size_t)row * f;
+  v4f v[VEC];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int i = (j * kWave + lane) * 4;
+    v[j] = i < f ? *reinterpret_cast<const v4f *>(x + i) : v4f{0.f, 0.f, 0.f, 0.f};
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+  }
+  amax = wave_max(amax);
+  float r = 1.0f, s = 1.0f;
+  if (amax != 0.0f) {
+    r = kE4m3Max / amax;
+    s = amax / kE4m3Max;
+  }
+  uint8_t *q = hq + (size_t)row * f;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int i = (j * kWave + lane) * 4;
+    if (i < f) *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r);
+  }
+  if (lane == 0) sh[row] = s;
+}
+
 // ------------------------------------------------------------------ combine
 // out[t] = sum_j w[t,j] * y[inv[t,j]] over valid slots in order, then + the
 // shared experts' rows in order; each y row is the sum of its K-split slabs
@@ -399,11 +436,27 @@ __device__ __forceinline__ void combine_chunk(const RowSpace &rs, const float *_
     for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const v4f *>(y + s * slab + row * d + c);
     return v;
   };
+  // slots in groups of 8: all their rows are fetched before any is added,
+  // and the sum still runs in slot order
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < K; ++j) {
-    const int p = t * K + j;
-    if (ids[p] < 0) continue;
-    acc += w[p] * yrow((size_t)inv[p]);
+  constexpr int G = 8;
+  for (int j0 = 0; j0 < K; j0 += G) {
+    int row[G];
+    float wt[G];
+    v4f yv[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = j0 + u, p = t * K + j;
+      const bool ok = j < K && ids[p] >= 0;
+      row[u] = ok ? inv[p] : -1;
+      wt[u] = ok ? w[p] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (row[u] >= 0) yv[u] = yrow((size_t)row[u]);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (row[u] >= 0) acc += wt[u] * yv[u];
   }
   for (int s = 0; s < rs.S; ++s) acc += yrow((size_t)rs.capacity + (size_t)s * rs.T + t);
   *reinterpret_cast<v4f *>(out + (size_t)t * d + c) = acc;

@@ -48,6 +48,13 @@ constexpr int64_t kRouterDotMax = 1 << 16;
 hipError_t launch_route_logits(const float *x, const float *w_router, const float *bias, int32_t T,
                                int32_t d, int32_t E, float *logits, uint8_t *xq, float *sx,
                                hipStream_t stream);
+// Router logits + quantisation of x + top-k in one launch (decode-sized
+// batches: route_fused_applies(T, E)); the logits equal launch_router's.
+bool route_fused_applies(int32_t T, int32_t E);
+hipError_t launch_route_topk_fused(const float *x, const float *w_router, const float *bias,
+                                   int32_t T, int32_t d, int32_t E, int32_t k_max,
+                                   const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
+                                   int32_t *ids, float *w, hipStream_t stream);
 hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
                        const int32_t *k_per_token, int32_t *ids, float *w, hipStream_t stream);
 // items/n_items/row_chunk: optional work list for the expert stages (row_chunk
@@ -64,12 +71,13 @@ int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int
 // five, two workgroups share a CU).
 constexpr int kGemmMaxWaves = 8;
 constexpr int kGemmMaxThreads = (kGemmMaxWaves + 1) * 64;
-// 256-row passes (msub 16): two loader waves, at most six compute waves.
+// 256-row passes (msub 16, two loader waves) and four weight operands per
+// wave (nb 4) use up to 256 VGPRs: at most eight waves per workgroup.
+constexpr int kGemmMaxThreadsWide = 8 * 64;
 constexpr int kGemmMaxWaves16 = 6;
-constexpr int kGemmMaxThreads16 = (kGemmMaxWaves16 + 2) * 64;
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
-                          hipStream_t stream);
+                          int32_t nb, hipStream_t stream);
 // Per-row e4m3 requantisation of h (real rows only): hq codes, sh = amax/448.
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream);
@@ -79,12 +87,12 @@ hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float
 // count actually used is down_splits_used(f, msub, splits).
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
-                       int32_t waves, hipStream_t stream);
+                       int32_t waves, int32_t nb, hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
 // Final K-split count and bytes per split for a requested split count.
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
                          int32_t *ksplit);
-constexpr int kDownChannelsPerWave = 32;  // output channels per down-projection wave
+constexpr int kDownChannelsPerWave = 32;  // output channels per down-projection wave (nb 2)
 // out from y slabs summed in split order.
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
                           const float *w, const int32_t *inv_pairs, float *out,

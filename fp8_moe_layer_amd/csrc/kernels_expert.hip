@@ -41,7 +41,7 @@ namespace fp8moe {
 // row passes of up to 128 rows two workgroups share a CU; otherwise one
 // workgroup per CU (256-row passes use 130 KB of LDS and up to 256 VGPRs).
 template <int MSUB, int NB, bool GATEUP>
-__global__ __launch_bounds__(MSUB > 8 ? kGemmMaxThreads16 : kGemmMaxThreads) void wsgemm_kernel(
+__global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMaxThreads) void wsgemm_kernel(
     GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t abuf[Chunk<MSUB>::LDS];
   wsgemm_tile<MSUB, NB, GATEUP>(g, blockIdx.x, abuf);
@@ -160,8 +160,8 @@ static int grid_items(const RowSpace &rs) { return rs.items ? rs.max_items : rs.
 template <int MSUB, int NB, bool GATEUP>
 static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
   const int N = GATEUP ? g.rs.f : g.rs.d;
-  const int ch_wave = GATEUP ? 16 : 16 * NB;
-  const int maxw = MSUB > 8 ? kGemmMaxWaves16 : kGemmMaxWaves;
+  const int ch_wave = GATEUP ? 8 * NB : 16 * NB;
+  const int maxw = MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide / 64 - Chunk<MSUB>::LOADERS : kGemmMaxWaves;
   const int wv = waves < 1 ? 1 : waves > maxw ? maxw : waves;
   const int n_tiles = (N + wv * ch_wave - 1) / (wv * ch_wave);
   const int blocks = grid_items(g.rs) * n_tiles * g.splits;
@@ -173,20 +173,38 @@ static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
 
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
-                          hipStream_t stream) {
+                          int32_t nb, hipStream_t stream) {
   GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
   if (msub >= 16) return launch_ws<16, 2, true>(g, waves, stream);
+  if (nb >= 4) {
+    if (msub >= 8) return launch_ws<8, 4, true>(g, waves, stream);
+    if (msub >= 4) return launch_ws<4, 4, true>(g, waves, stream);
+    if (msub >= 2) return launch_ws<2, 4, true>(g, waves, stream);
+    return launch_ws<1, 4, true>(g, waves, stream);
+  }
   if (msub >= 8) return launch_ws<8, 2, true>(g, waves, stream);
   if (msub >= 4) return launch_ws<4, 2, true>(g, waves, stream);
   if (msub >= 2) return launch_ws<2, 2, true>(g, waves, stream);
   return launch_ws<1, 2, true>(g, waves, stream);
 }
 
+// Rows of up to 4096 values: a wave per row, four rows per workgroup.
+__global__ __launch_bounds__(256) void requant_wave_kernel(RowSpace rs, const float *__restrict__ h,
+                                                           uint8_t *__restrict__ hq,
+                                                           float *__restrict__ sh) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rs.capacity + rs.S * rs.T) return;
+  requant_row_wave<16>(rs, h, hq, sh, row, threadIdx.x & 63);
+}
+
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream) {
   const int rows_total = rs.capacity + rs.S * rs.T;
   if (rows_total == 0) return hipSuccess;
-  requant_kernel<<<rows_total, kRowThreads, 0, stream>>>(rs, h, hq, sh);
+  if (rs.f <= 4096)
+    requant_wave_kernel<<<(rows_total + 3) / 4, 256, 0, stream>>>(rs, h, hq, sh);
+  else
+    requant_kernel<<<rows_total, kRowThreads, 0, stream>>>(rs, h, hq, sh);
   return hipGetLastError();
 }
 
@@ -207,7 +225,7 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
 
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
-                       int32_t waves, hipStream_t stream) {
+                       int32_t waves, int32_t nb, hipStream_t stream) {
   if (h32) {
     GemmArgs g{rs, nullptr, nullptr, h32, w, y, 1, rs.f};
     const int blocks = grid_items(rs) * ((rs.d + 63) >> 6);
@@ -218,9 +236,13 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   int32_t ksplit;
   down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
-  // 32 channels per wave: the activation rows each workgroup loads are
-  // shared by twice the weight bytes.
   if (msub >= 16) return launch_ws<16, 2, false>(g, waves, stream);
+  if (nb >= 4) {
+    if (msub >= 8) return launch_ws<8, 4, false>(g, waves, stream);
+    if (msub >= 4) return launch_ws<4, 4, false>(g, waves, stream);
+    if (msub >= 2) return launch_ws<2, 4, false>(g, waves, stream);
+    return launch_ws<1, 4, false>(g, waves, stream);
+  }
   if (msub >= 8) return launch_ws<8, 2, false>(g, waves, stream);
   if (msub >= 4) return launch_ws<4, 2, false>(g, waves, stream);
   if (msub >= 2) return launch_ws<2, 2, false>(g, waves, stream);

@@ -1,5 +1,6 @@
-// kernels_permute.hip -- the permutation (dispatch on one device) as one
-// 16-wave workgroup; the algorithm is in permute_dev.hpp.
+// kernels_permute.hip -- the permutation (dispatch on one device): one
+// 16-wave workgroup for decode-sized batches, three launches over slices of
+// the pairs for large ones; the algorithm is in permute_dev.hpp.
 #include "common.hpp"
 #include "internal.hpp"
 #include "permute_dev.hpp"
@@ -20,6 +21,78 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
                             inv_pairs, n_blocks, items, n_items, row_chunk, T, S, lds);
 }
 
+// ------------------------------------------------------------------ many workgroups
+__global__ __launch_bounds__(kSliceWaves * kWave) void permute_count_kernel(
+    const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ inv_pairs) {
+  __shared__ int cnt[kSliceWaves * kMaxExperts];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int b0, b1;
+  slice_range(P, blockIdx.x, b0, b1);
+  for (int i = tid; i < kSliceWaves * E; i += kSliceWaves * kWave) cnt[i] = 0;
+  __syncthreads();
+  const int per = (b1 - b0 + kSliceWaves - 1) / kSliceWaves;
+  const int w0 = min(b1, b0 + wave * per), w1 = min(b1, w0 + per);
+  slice_count(ids, w0, w1, expert_bits(E), cnt + wave * E, lane);
+  __syncthreads();
+  for (int e = tid; e < E; e += kSliceWaves * kWave) {
+    int c = 0;
+    for (int w = 0; w < kSliceWaves; ++w) c += cnt[w * E + e];
+    inv_pairs[b0 + e] = c;  // this slice's count of expert e
+  }
+}
+
+__global__ __launch_bounds__(1024) void permute_layout_kernel(
+    int P, int E, int bm, int capacity, int32_t *__restrict__ sorted_pairs,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ block_expert,
+    int32_t *__restrict__ inv_pairs, int32_t *__restrict__ n_blocks, WorkItem *__restrict__ items,
+    int32_t *__restrict__ n_items, int row_chunk, int T, int S) {
+  __shared__ int tot[kMaxExperts], off[kMaxExperts + 1], item_off[kMaxExperts + 1];
+  const int ns = permute_slices(P);
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int run = 0;  // exclusive prefix over slices
+    for (int b = 0; b < ns; ++b) {
+      const int c = inv_pairs[b * kSlice + e];
+      inv_pairs[b * kSlice + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  build_layout<1024>(tot, off, item_off, P, E, bm, capacity, sorted_pairs, expert_offsets,
+                     block_expert, n_blocks, items, n_items, row_chunk, T, S);
+  for (int e = threadIdx.x; e < E; e += 1024)
+    for (int b = 0; b < ns; ++b) inv_pairs[b * kSlice + e] += off[e];  // first row of slice b
+}
+
+__global__ __launch_bounds__(kSliceWaves * kWave) void permute_scatter_kernel(
+    const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ sorted_pairs,
+    int32_t *__restrict__ inv_pairs) {
+  __shared__ int cnt[kSliceWaves * kMaxExperts], base[kMaxExperts];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int b0, b1;
+  slice_range(P, blockIdx.x, b0, b1);
+  for (int e = tid; e < E; e += kSliceWaves * kWave) base[e] = inv_pairs[b0 + e];
+  for (int i = tid; i < kSliceWaves * E; i += kSliceWaves * kWave) cnt[i] = 0;
+  __syncthreads();  // the slice's bases are read before its inv_pairs entries are written
+  const int per = (b1 - b0 + kSliceWaves - 1) / kSliceWaves;
+  const int w0 = min(b1, b0 + wave * per), w1 = min(b1, w0 + per);
+  const int nbits = expert_bits(E);
+  slice_count(ids, w0, w1, nbits, cnt + wave * E, lane);
+  __syncthreads();
+  for (int e = tid; e < E; e += kSliceWaves * kWave) {
+    int s = base[e];
+    for (int w = 0; w < kSliceWaves; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = s;
+      s += c;
+    }
+  }
+  __syncthreads();
+  slice_scatter(ids, w0, w1, nbits, cnt + wave * E, sorted_pairs, inv_pairs, lane);
+}
+
+constexpr int kManySlices = 4;  // at least this many slices: the multi-workgroup path
+
 int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int32_t n_shared,
                        int32_t row_chunk) {
   const int64_t cap = (int64_t)T * k_max + (int64_t)E * (block_m - 1);
@@ -34,7 +107,18 @@ hipError_t launch_permute(const int32_t *ids, int32_t T, int32_t E, int32_t k_ma
                           int32_t *block_expert, int32_t *inv_pairs, int32_t *n_blocks,
                           WorkItem *items, int32_t *n_items, int32_t row_chunk, int32_t n_shared,
                           hipStream_t stream) {
-  permute_kernel<<<1, kPermThreads, 0, stream>>>(ids, T * k_max, E, block_m, capacity, sorted_pairs,
+  const int P = T * k_max;
+  const int ns = permute_slices(P);
+  if (ns >= kManySlices) {
+    permute_count_kernel<<<ns, kSliceWaves * kWave, 0, stream>>>(ids, P, E, inv_pairs);
+    permute_layout_kernel<<<1, 1024, 0, stream>>>(P, E, block_m, capacity, sorted_pairs,
+                                                  expert_offsets, block_expert, inv_pairs, n_blocks,
+                                                  items, n_items, row_chunk, T, n_shared);
+    permute_scatter_kernel<<<ns, kSliceWaves * kWave, 0, stream>>>(ids, P, E, sorted_pairs,
+                                                                   inv_pairs);
+    return hipGetLastError();
+  }
+  permute_kernel<<<1, kPermThreads, 0, stream>>>(ids, P, E, block_m, capacity, sorted_pairs,
                                                  expert_offsets, block_expert, inv_pairs, n_blocks,
                                                  items, n_items, row_chunk, T, n_shared);
   return hipGetLastError();

@@ -53,6 +53,45 @@ __global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict
   router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, wid - t * E, threadIdx.x & 63);
 }
 
+// Decode-sized batches: one workgroup per token computes its E logits (one
+// wave per expert at a time, the arithmetic of router_dot_wave, so the
+// logits equal those of moe_router_logits), quantises the token (expert 0's
+// wave) and, from the logits kept in LDS, picks its top-k with softmax
+// weights -- routing in one launch.
+__global__ __launch_bounds__(1024) void route_token_kernel(
+    const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
+    int d, int E, int k_max, const int32_t *__restrict__ kpt, float *__restrict__ logits,
+    uint8_t *__restrict__ xq, float *__restrict__ sx, int32_t *__restrict__ ids,
+    float *__restrict__ w) {
+  __shared__ float ls[kMaxExperts];
+  const int t = blockIdx.x, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int e = wave; e < E; e += nw) {
+    const float lg = router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, e, lane);
+    if (lane == 0) ls[e] = lg;
+  }
+  __syncthreads();
+  if (wave == 0)
+    topk_row_wave(ls, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+                  w + (size_t)t * k_max, lane);
+}
+
+// One workgroup per token pays off while a token's experts fit one wave each.
+bool route_fused_applies(int32_t T, int32_t E) {
+  return E <= 16 && (int64_t)T * E <= kRouterDotMax;
+}
+
+hipError_t launch_route_topk_fused(const float *x, const float *w_router, const float *bias,
+                                   int32_t T, int32_t d, int32_t E, int32_t k_max,
+                                   const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
+                                   int32_t *ids, float *w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int nw = E < 16 ? E : 16;
+  route_token_kernel<<<T, nw * 64, 0, stream>>>(x, w_router, bias, d, E, k_max, kpt, logits, xq,
+                                                sx, ids, w);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void router_mfma_kernel(const float *__restrict__ x,
                                                           const float *__restrict__ wr,
                                                           const float *__restrict__ bias, int T,

@@ -49,35 +49,11 @@ __device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int nbit
   return m;
 }
 
-// Every thread of the workgroup (NW waves) calls this; lds holds
-// permute_lds_ints<NW>() ints.  items may be nullptr (no work list).
-template <int NW>
-__device__ __forceinline__ void permute_block(
-    const int32_t *__restrict__ ids, int P, int E, int bm, int capacity,
-    int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ expert_offsets,
-    int32_t *__restrict__ block_expert, int32_t *__restrict__ inv_pairs,
-    int32_t *__restrict__ n_blocks, WorkItem *__restrict__ items, int32_t *__restrict__ n_items,
-    int row_chunk, int T, int S, int *lds) {
-  int *cnt = lds;                          // [NW][E] per (wave, expert) count, then base
-  int *tot = cnt + NW * kMaxExperts;       // [E]
-  int *off = tot + kMaxExperts;            // [E+1]
-  int *item_off = off + kMaxExperts + 1;   // [E+1]
-  constexpr int NT = NW * kWave;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sentinel = P;
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
+// Pass 1 over one wave's slice [b0, b1): adds each expert's count to my[e].
+__device__ __forceinline__ void slice_count(const int32_t *__restrict__ ids, int b0, int b1,
+                                            int nbits, int *my, int lane) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  for (int i = tid; i < NW * E; i += NT) cnt[i] = 0;
-  __syncthreads();
-
-  const int per = (P + NW - 1) / NW;
-  const int b0 = min(P, wave * per), b1 = min(P, b0 + per);
-  int *my = cnt + wave * E;
-
-  // pass 1: per-wave counts (the slice's ids are fetched kBatch steps at a
-  // time so the loads overlap instead of serialising the walk)
+  // the slice's ids are fetched kBatch steps at a time so the loads overlap
   for (int base = b0; base < b1; base += kWave * kBatch) {
     int ev[kBatch];
 #pragma unroll
@@ -94,20 +70,65 @@ __device__ __forceinline__ void permute_block(
       __builtin_amdgcn_wave_barrier();
     }
   }
-  __syncthreads();
+}
 
-  // exclusive prefix over waves per expert; totals
-  for (int e = tid; e < E; e += NT) {
-    int s = 0;
-    for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = s;
-      s += c;
+// Pass 2 over the same slice: pair p of expert e goes to row my[e] + (its
+// rank among the equal experts before it in the step); my[e] advances.
+__device__ __forceinline__ void slice_scatter(const int32_t *__restrict__ ids, int b0, int b1,
+                                              int nbits, int *my, int32_t *__restrict__ sorted_pairs,
+                                              int32_t *__restrict__ inv_pairs, int lane) {
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = b0; base < b1; base += kWave * kBatch) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = base + u * kWave + lane;
+      ev[u] = p < b1 ? ids[p] : -1;
     }
-    tot[e] = s;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = base + u * kWave + lane;
+      const int e = ev[u];
+      const bool valid = e >= 0;
+      const uint64_t m = same_expert_mask(e, valid, nbits);
+      if (valid) {
+        const int rank = __popcll(m & lt_mask);
+        const int row = my[e] + rank;
+        sorted_pairs[row] = p;
+        inv_pairs[p] = row;
+        // the leader's update is ordered after every lane's read above (same wave)
+        __builtin_amdgcn_wave_barrier();
+        if (rank == 0) my[e] += __popcll(m);
+      } else if (p < b1) {
+        inv_pairs[p] = -1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
-  __syncthreads();
+}
 
+__device__ __forceinline__ int expert_bits(int E) {
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
+
+// From the per-expert totals tot[E] (LDS): padded segment offsets off[E+1]
+// (LDS and expert_offsets), the block table, the padding sentinels, n_blocks
+// and the work list.  Every thread of the workgroup (NT of them) calls this;
+// it ends with a workgroup barrier.
+template <int NT>
+__device__ __forceinline__ void build_layout(const int *tot, int *off, int *item_off, int P, int E,
+                                             int bm, int capacity,
+                                             int32_t *__restrict__ sorted_pairs,
+                                             int32_t *__restrict__ expert_offsets,
+                                             int32_t *__restrict__ block_expert,
+                                             int32_t *__restrict__ n_blocks,
+                                             WorkItem *__restrict__ items,
+                                             int32_t *__restrict__ n_items, int row_chunk, int T,
+                                             int S) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sentinel = P;
   // exclusive scan of padded totals; work-list offsets
   if (wave == 0) {
     int run = 0, irun = 0;
@@ -160,35 +181,72 @@ __device__ __forceinline__ void permute_block(
     }
     if (tid == 0) *n_items = item_off[E] + S * per_shared;
   }
+  __syncthreads();
+}
 
-  // pass 2: scatter (rows from base + running count + rank in the step)
-  for (int base = b0; base < b1; base += kWave * kBatch) {
-    int ev[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = base + u * kWave + lane;
-      ev[u] = p < b1 ? ids[p] : -1;
+// Every thread of the workgroup (NW waves) calls this; lds holds
+// permute_lds_ints<NW>() ints.  items may be nullptr (no work list).
+template <int NW>
+__device__ __forceinline__ void permute_block(
+    const int32_t *__restrict__ ids, int P, int E, int bm, int capacity,
+    int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ block_expert, int32_t *__restrict__ inv_pairs,
+    int32_t *__restrict__ n_blocks, WorkItem *__restrict__ items, int32_t *__restrict__ n_items,
+    int row_chunk, int T, int S, int *lds) {
+  int *cnt = lds;                          // [NW][E] per (wave, expert) count, then base
+  int *tot = cnt + NW * kMaxExperts;       // [E]
+  int *off = tot + kMaxExperts;            // [E+1]
+  int *item_off = off + kMaxExperts + 1;   // [E+1]
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nbits = expert_bits(E);
+
+  for (int i = tid; i < NW * E; i += NT) cnt[i] = 0;
+  __syncthreads();
+
+  const int per = (P + NW - 1) / NW;
+  const int b0 = min(P, wave * per), b1 = min(P, b0 + per);
+  int *my = cnt + wave * E;
+  slice_count(ids, b0, b1, nbits, my, lane);
+  __syncthreads();
+
+  // exclusive prefix over waves per expert; totals
+  for (int e = tid; e < E; e += NT) {
+    int s = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = s;
+      s += c;
     }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int p = base + u * kWave + lane;
-      const int e = ev[u];
-      const bool valid = e >= 0;
-      const uint64_t m = same_expert_mask(e, valid, nbits);
-      if (valid) {
-        const int rank = __popcll(m & lt_mask);
-        const int row = off[e] + my[e] + rank;
-        sorted_pairs[row] = p;
-        inv_pairs[p] = row;
-        // the leader's update is ordered after every lane's read above (same wave)
-        __builtin_amdgcn_wave_barrier();
-        if (rank == 0) my[e] += __popcll(m);
-      } else if (p < b1) {
-        inv_pairs[p] = -1;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
+    tot[e] = s;
   }
+  __syncthreads();
+  build_layout<NT>(tot, off, item_off, P, E, bm, capacity, sorted_pairs, expert_offsets,
+                   block_expert, n_blocks, items, n_items, row_chunk, T, S);
+
+  // pass 2: scatter (rows from segment start + wave base + running count)
+  for (int e = lane; e < E; e += kWave) my[e] += off[e];
+  __builtin_amdgcn_wave_barrier();
+  slice_scatter(ids, b0, b1, nbits, my, sorted_pairs, inv_pairs, lane);
+}
+
+// ------------------------------------------------------------------ many workgroups
+// Large batches: the pairs are cut into slices of at least kSlice pairs (the
+// last one takes the remainder), one 4-wave workgroup each.  Counting,
+// then one workgroup scanning the slices' counts and laying out the
+// segments, then the scatter -- the same rows as permute_block.  A slice's
+// counts and then its base rows are kept in the first E entries of its own
+// range of inv_pairs, which only its own workgroup overwrites, after reading
+// them.
+constexpr int kSlice = 1024;  // >= kMaxExperts: a slice's first E entries hold its counts
+constexpr int kSliceWaves = 4;
+
+__host__ __device__ inline int permute_slices(int P) { return P / kSlice; }
+
+__device__ __forceinline__ void slice_range(int P, int blk, int &b0, int &b1) {
+  const int ns = permute_slices(P);
+  b0 = blk * kSlice;
+  b1 = blk == ns - 1 ? P : b0 + kSlice;
 }
 
 }  // namespace fp8moe

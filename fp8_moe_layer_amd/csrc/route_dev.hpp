@@ -16,12 +16,14 @@ namespace fp8moe {
 // The wave of expert 0 also quantises its token's row (it has read it).
 constexpr int kDotVec = 8;  // float4 per lane per round: d <= 2048 in one round
 
-__device__ __forceinline__ void router_dot_wave(const float *__restrict__ x,
-                                                const float *__restrict__ wr,
-                                                const float *__restrict__ bias, int d, int E,
-                                                float *__restrict__ logits,
-                                                uint8_t *__restrict__ xq, float *__restrict__ sx,
-                                                int t, int e, int lane) {
+// Returns the logit (in every lane; the butterfly sum is bitwise the same
+// in all lanes).
+__device__ __forceinline__ float router_dot_wave(const float *__restrict__ x,
+                                                 const float *__restrict__ wr,
+                                                 const float *__restrict__ bias, int d, int E,
+                                                 float *__restrict__ logits,
+                                                 uint8_t *__restrict__ xq, float *__restrict__ sx,
+                                                 int t, int e, int lane) {
   const float *xr = x + (size_t)t * d;
   const float *w = wr + (size_t)e * d;
   float acc = 0.0f, amax = 0.0f;
@@ -44,7 +46,8 @@ __device__ __forceinline__ void router_dot_wave(const float *__restrict__ x,
     }
   }
   acc = wave_sum(acc);
-  if (lane == 0) logits[(size_t)t * E + e] = bias ? acc + bias[e] : acc;
+  const float logit = bias ? acc + bias[e] : acc;
+  if (lane == 0) logits[(size_t)t * E + e] = logit;
   if (e == 0 && xq) {
     amax = wave_max(amax);
     float r = 1.0f, s = 1.0f;
@@ -59,6 +62,7 @@ __device__ __forceinline__ void router_dot_wave(const float *__restrict__ x,
     }
     if (lane == 0) sx[t] = s;
   }
+  return logit;
 }
 
 // ------------------------------------------------------------------ router, tiled
@@ -159,18 +163,17 @@ __device__ __forceinline__ uint64_t route_key(float l, int e) {
 
 constexpr int kTopkSlots = kMaxExperts / kWave;
 
-__device__ __forceinline__ void topk_token_wave(const float *__restrict__ logits, int T, int E,
-                                                int k_max, const int32_t *__restrict__ kpt,
-                                                int32_t *__restrict__ ids, float *__restrict__ w,
-                                                int t, int lane) {
-  const float *l = logits + (size_t)t * E;
+// l: the token's E logits (global memory or LDS); writes the token's k_max
+// slots of ids / w.
+__device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, int kt,
+                                              int32_t *__restrict__ ids_row,
+                                              float *__restrict__ w_row, int lane) {
   uint64_t key[kTopkSlots];
 #pragma unroll
   for (int c = 0; c < kTopkSlots; ++c) {
     int e = lane + c * kWave;
     key[c] = e < E ? route_key(l[e], e) : 0ull;
   }
-  const int kt = kpt ? kpt[t] : k_max;
   float m = 0.0f, z = 0.0f, my_eps = 0.0f;
   int my_id = -1;
   for (int j = 0; j < kt; ++j) {
@@ -194,10 +197,18 @@ __device__ __forceinline__ void topk_token_wave(const float *__restrict__ logits
     }
   }
   if (lane < k_max) {
-    const size_t o = (size_t)t * k_max + lane;
-    ids[o] = lane < kt ? my_id : -1;
-    w[o] = lane < kt ? my_eps / z : 0.0f;
+    ids_row[lane] = lane < kt ? my_id : -1;
+    w_row[lane] = lane < kt ? my_eps / z : 0.0f;
   }
+}
+
+__device__ __forceinline__ void topk_token_wave(const float *__restrict__ logits, int T, int E,
+                                                int k_max, const int32_t *__restrict__ kpt,
+                                                int32_t *__restrict__ ids, float *__restrict__ w,
+                                                int t, int lane) {
+  (void)T;
+  topk_row_wave(logits + (size_t)t * E, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+                w + (size_t)t * k_max, lane);
 }
 
 }  // namespace fp8moe

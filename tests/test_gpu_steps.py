@@ -130,7 +130,9 @@ def test_topk_bit_exact(T, E, k, var):
 @pytest.mark.parametrize("T,E,k,bm,var", [(16, 8, 2, 16, False), (1, 8, 2, 16, False),
                                           (256, 8, 2, 64, False), (64, 128, 8, 16, False),
                                           (1000, 512, 32, 32, True), (513, 64, 6, 1, False),
-                                          (8192, 64, 6, 128, False), (3, 512, 4, 16, True)])
+                                          (8192, 64, 6, 128, False), (3, 512, 4, 16, True),
+                                          (2053, 64, 8, 16, False), (4096, 128, 8, 16, False),
+                                          (5000, 512, 8, 1, True)])
 def test_permute_bit_exact(T, E, k, bm, var):
     rng = np.random.default_rng(T * 3 + E)
     l = rng.standard_normal((T, E)).astype(np.float32)
