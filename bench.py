@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     p.add_argument("--sweep", action="store_true", help="also time the config's batch sweep")
     p.add_argument("--no-requant", action="store_true")
+    p.add_argument("--zipf-sweep", action="store_true",
+                   help="qwen3: also time T=64 at several Zipf router biases (distinct experts 16..128)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -192,6 +194,11 @@ def main():
     d, f, E = spec.d, spec.f, spec.E
     expert_bytes = 3 * f * d + 8 * f + 4 * d
 
+    def clone_weights():
+        return fp8.DeviceWeights(*[None if t is None else t.clone() for t in
+                                   (dw.w_gate, dw.w_up, dw.s_gate, dw.s_up, dw.w_down, dw.s_down,
+                                    dw.ws_gate, dw.ws_up, dw.ss_gate, dw.ss_up, dw.ws_down, dw.ss_down)])
+
     def layers_for(Tn):
         """Rotated weight copies so that one step's active weights x copies >= 1 GB
         (the active experts counted from a first forward at this batch)."""
@@ -204,10 +211,7 @@ def main():
         copies = max(1, min(16, math.ceil(1e9 / (active * expert_bytes))))
         out = [base]
         for _ in range(copies - 1):
-            c = fp8.DeviceWeights(*[None if t is None else t.clone() for t in
-                                    (dw.w_gate, dw.w_up, dw.s_gate, dw.s_up, dw.w_down, dw.s_down,
-                                     dw.ws_gate, dw.ws_up, dw.ss_gate, dw.ss_up, dw.ws_down, dw.ss_down)])
-            out.append(fp8.MoELayer(c, w_router, spec.k, bias, no_requant=args.no_requant))
+            out.append(fp8.MoELayer(clone_weights(), w_router, spec.k, bias, no_requant=args.no_requant))
         return out
 
     stream = torch.cuda.current_stream()
@@ -247,6 +251,19 @@ def main():
     ms, x, kpt, out, ids = time_layer(T, args.steps, args.warmup, layers)
     tokens_per_s = T / (ms * 1e-3)
     log(f"T={T}: {ms * 1e3:.1f} us/step, {tokens_per_s:.4g} tokens/s, {len(layers)} weight copies")
+
+    # ---- per-step distribution (events around each step only)
+    pev = HipEvents(args.steps + 1)
+    pev.record(0, sh)
+    for i in range(args.steps):
+        layers[i % len(layers)].forward(x, k_per_token=kpt, out=out, topk_ids=ids)
+        pev.record(i + 1, sh)
+    torch.cuda.synchronize()
+    per_step = sorted(pev.elapsed_ms(i, i + 1) * 1e3 for i in range(args.steps))
+    pev.close()
+    pct = lambda q: round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 2)
+    step_us = {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9)}
+    log(f"per-step us: {step_us}")
 
     # ---- per-stage timing (second pass, same inputs)
     nst = fp8.N_STAGE_EVENTS
@@ -293,6 +310,42 @@ def main():
                               "mfma_frac": round(fl / (mst * 1e-3) / PEAK_FP8, 4), "weight_copies": len(lay)}
             log(f"sweep T={Tn}: {sweep[str(Tn)]}")
             del lay
+
+    # ---- Qwen3-shaped decode at several router biases (distinct active experts)
+    zipf = None
+    if args.zipf_sweep and cfg == "qwen3":
+        zipf = []
+        zcopies = []
+        for alpha in (0.0, 1.0, 1.5, 2.0, 3.0, 4.0):
+            zs = wl.SPECS[cfg].with_(T=64, bias_param=alpha)
+            zri = wl.routing_inputs(zs, args.seed)
+            zb = None if zri.router_bias is None else zri.router_bias.to(dev)
+            zx = zri.x.to(dev)
+            base = fp8.MoELayer(dw, zri.w_router.to(dev), zs.k, zb)
+            zid = torch.empty((64, zs.k), dtype=torch.int32, device=dev)
+            base.forward(zx, topk_ids=zid)
+            zi = zid.cpu().numpy()
+            Dz = int(len(np.unique(zi[zi >= 0])))
+            copies = max(1, min(16, math.ceil(1e9 / (Dz * expert_bytes))))
+            while len(zcopies) < copies - 1:
+                zcopies.append(clone_weights())
+            lays = [base] + [fp8.MoELayer(c, zri.w_router.to(dev), zs.k, zb) for c in zcopies[:copies - 1]]
+            zout = torch.empty((64, d), dtype=torch.float32, device=dev)
+            for i in range(args.warmup):
+                lays[i % len(lays)].forward(zx, out=zout, topk_ids=zid)
+            ev = HipEvents(2)
+            torch.cuda.synchronize()
+            ev.record(0, sh)
+            for i in range(args.steps):
+                lays[i % len(lays)].forward(zx, out=zout, topk_ids=zid)
+            ev.record(1, sh)
+            torch.cuda.synchronize()
+            zms = ev.elapsed_ms(0, 1) / args.steps
+            ev.close()
+            zbytes = Dz * expert_bytes + E * d * 4 + 2 * 64 * d * 4
+            zipf.append({"alpha": alpha, "distinct_experts": Dz, "us": round(zms * 1e3, 1),
+                         "hbm_frac": round(zbytes / (zms * 1e-3) / PEAK_HBM, 4), "weight_copies": len(lays)})
+            log(f"zipf alpha={alpha}: {zipf[-1]}")
 
     # ---- CPU oracle on a bounded sample (same inputs), plus a parity check
     cpu = None
@@ -364,11 +417,14 @@ def main():
         "cpu_baseline": cpu,
         "layer": {"alg_bytes": layer_bytes, "hbm_frac": round(layer_bytes / (ms * 1e-3) / PEAK_HBM, 4),
                   "fp8_flops": flops, "mfma_frac": round(flops / (ms * 1e-3) / PEAK_FP8, 5)},
+        "step_us": step_us,
         "stages_us": stages_us,
         "parity": parity,
     }
     if sweep:
         res["sweep"] = sweep
+    if zipf:
+        res["zipf_sweep"] = zipf
     print(json.dumps(res), flush=True)
 
 
