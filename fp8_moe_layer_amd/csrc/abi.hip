@@ -119,6 +119,22 @@ double expected_active(const moe_dims *d) {
   return E * (1.0 - pow(1.0 - (double)d->k_max / E, (double)d->T));
 }
 
+// Row-pass height for work items that outgrow 16*msub rows.  A token picks
+// an expert at most once, so routing can send up to the whole batch to one
+// expert; items are cut at 16*msub_big rows, msub_big covering the batch
+// where it can (at most 8).  Equal to msub where one shape serves (or the
+// row pass is forced).
+int32_t choose_msub_big(const moe_dims *d, int32_t msub) {
+  if (msub >= 8) return msub;
+  const int forced = env_int("FP8MOE_MSUB_BIG", 0);  // tile-tuning override
+  if (forced == 2 || forced == 4 || forced == 8) return forced > msub ? forced : msub;
+  if (env_int("FP8MOE_MSUB", 0) > 0) return msub;
+  const int64_t most = ((int64_t)d->T + d->block_m - 1) / d->block_m * d->block_m;
+  int32_t m = msub;
+  while (m < 8 && 16 * (int64_t)m < most) m <<= 1;
+  return m;
+}
+
 // Expected work items of the grouped GEMMs (rows cut into 16*msub chunks).
 double expected_items(const moe_dims *d, int32_t msub) {
   const double chunk = 16.0 * msub;
@@ -194,7 +210,7 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
 struct Layout {
   size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
       hq, sh, y, total;
-  int32_t capacity, rows_total, max_items, row_chunk, msub, splits;
+  int32_t capacity, rows_total, max_items, row_chunk, msub, msub_big, splits;
   GemmPlan gu, dn;
 };
 
@@ -205,9 +221,10 @@ Layout layout_of(const moe_dims *d) {
   L.capacity = (int32_t)capacity_of(d->T, d->E, d->k_max, d->block_m);
   L.rows_total = L.capacity + d->n_shared * d->T;
   L.msub = choose_msub(d);
-  L.row_chunk = 16 * L.msub;
   L.gu = plan_gemm(d, L.msub, true);
   L.dn = plan_gemm(d, L.msub, false);
+  L.msub_big = (L.gu.nb == 2 && L.dn.nb == 2) ? choose_msub_big(d, L.msub) : L.msub;
+  L.row_chunk = 16 * L.msub_big;
   L.splits = L.dn.splits;
   L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
   const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
@@ -395,7 +412,8 @@ moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
   const int32_t msub = choose_msub(dims);
   const GemmPlan gp = plan_gemm(dims, msub, true);
-  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub, gp.waves, gp.nb,
+  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub,
+                                gp.nb == 2 ? choose_msub_big(dims, msub) : msub, gp.waves, gp.nb,
                                 as_stream(stream)),
                  fn);
   return s ? s : ok();
@@ -418,7 +436,8 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
   const int32_t msub = choose_msub(dims);
   const GemmPlan dp = plan_gemm(dims, msub, false);
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
-                             msub, 1, dp.waves, dp.nb, as_stream(stream)),
+                             msub, dp.nb == 2 ? choose_msub_big(dims, msub) : msub, 1, dp.waves,
+                             dp.nb, as_stream(stream)),
                  fn);
   return s ? s : ok();
 }
@@ -532,17 +551,17 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   rs.max_items = L.max_items;
   const ExpertWeights ew = to_internal(w);
   mark(3);
-  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.gu.waves, L.gu.nb, st), "gate_up"))) return s;
+  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, st), "gate_up"))) return s;
   mark(4);
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.splits, L.dn.waves, L.dn.nb, st),
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, st),
                         "down")))
       return s;
   } else {
     mark(5);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, 1, L.dn.waves, L.dn.nb, st), "down")))
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, st), "down")))
       return s;
   }
   mark(6);

@@ -55,27 +55,74 @@ __device__ __forceinline__ v4f mfma_f16_16x16x32(v8h a, v8h b, v4f c) {
 }
 
 // ---------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Cross-lane steps inside each row of 16 lanes use DPP (a register operand
+// modifier, a few cycles) rather than ds_bpermute (a round trip through the
+// LDS crossbar); the four row results are then combined from v_readlane
+// values, identically in every lane.  All 64 lanes must be active.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each row
+constexpr int kDppRowShr = 0x110;     // + n: lane i reads lane i - n of its row (n = 1..15)
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(dpp_mov<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_mov(uint64_t v) {
+  const uint32_t lo = (uint32_t)dpp_mov<CTRL>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)dpp_mov<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ uint64_t readlane(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Butterfly inside each row of 16 (every lane of a row ends with the row's
+// result; op must be commutative), then the rows in the order (0,1),(2,3).
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_mov<kDppQuadXor1>(v));
+  v = op(v, dpp_mov<kDppQuadXor2>(v));
+  v = op(v, dpp_mov<kDppHalfMirror>(v));
+  v = op(v, dpp_mov<kDppMirror>(v));
+  return op(op(readlane(v, 0), readlane(v, 16)), op(readlane(v, 32), readlane(v, 48)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
+// The sum comes out bitwise the same in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 4, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 8, 0xf, 0xf, false);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -9,8 +9,9 @@
 //
 // Grouped GEMM schedule: weight-stationary, one workgroup per (work item,
 // tile of output channels[, K split]).  A work item is an expert and up to
-// 16*MSUB of its rows, so a decode-sized batch puts all of an expert's rows
-// in one item and each active expert's weights cross HBM exactly once.
+// 16*MSUB of its rows (16*ML with the two-shape kernel), so a decode-sized
+// batch puts all of an expert's rows in one item and each active expert's
+// weights cross HBM exactly once.
 //
 // Workgroup = 4 compute waves + 1 loader wave (320 lanes):
 //  - the loader wave gathers the item's activation rows (e4m3) into a ring of
@@ -45,6 +46,31 @@ __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMax
     GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t abuf[Chunk<MSUB>::LDS];
   wsgemm_tile<MSUB, NB, GATEUP>(g, blockIdx.x, abuf);
+}
+
+// Two row-pass shapes in one launch.  Work items are cut at 16*ML rows; an
+// item of at most 16*MS rows runs the MS shape (deeper weight prefetch, K
+// steps batched per LDS chunk), a longer one the ML shape.  Routing that
+// sends many of the batch's tokens to a few experts then still streams each
+// of their weights once, and the common short items keep the faster shape.
+// Both shapes have one loader wave and two weight operands per wave, hence
+// the same tiling of the grid.
+template <int MS, int ML, bool GATEUP>
+__global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
+  static_assert(MS < ML && Chunk<ML>::LOADERS == 1, "two row-pass shapes, one loader wave");
+  constexpr int LDS = Chunk<ML>::LDS > Chunk<MS>::LDS ? Chunk<ML>::LDS : Chunk<MS>::LDS;
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[LDS];
+  const int W = (int)(blockDim.x >> 6) - 1;
+  const int N = GATEUP ? g.rs.f : g.rs.d;
+  const int ch_wg = W * (GATEUP ? 16 : 32);
+  const int n_tiles = (N + ch_wg - 1) / ch_wg;
+  const int item_id = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / g.splits) / n_tiles);
+  int expert, row0, rows;
+  if (!resolve_item(g.rs, item_id, expert, row0, rows)) return;
+  if (__builtin_amdgcn_readfirstlane(rows) <= 16 * MS)
+    wsgemm_tile<MS, 2, GATEUP>(g, blockIdx.x, abuf);
+  else
+    wsgemm_tile<ML, 2, GATEUP>(g, blockIdx.x, abuf);
 }
 
 // ------------------------------------------------------------------ down, fp32 products
@@ -170,11 +196,39 @@ static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MS, int ML, bool GATEUP>
+static hipError_t launch_ws2(const GemmArgs &g, int waves, hipStream_t stream) {
+  const int N = GATEUP ? g.rs.f : g.rs.d;
+  const int ch_wave = GATEUP ? 16 : 32;
+  const int wv = waves < 1 ? 1 : waves > kGemmMaxWaves ? kGemmMaxWaves : waves;
+  const int n_tiles = (N + wv * ch_wave - 1) / (wv * ch_wave);
+  const int blocks = grid_items(g.rs) * n_tiles * g.splits;
+  if (blocks == 0) return hipSuccess;
+  wsgemm2_kernel<MS, ML, GATEUP><<<blocks, (wv + 1) * 64, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+// The two-shape kernel for (msub, msub_big), or false when that pair has none.
+template <bool GATEUP>
+static bool launch_pair(const GemmArgs &g, int msub, int msub_big, int waves, hipStream_t stream,
+                        hipError_t *err) {
+  switch (msub * 16 + msub_big) {
+    case 1 * 16 + 2: *err = launch_ws2<1, 2, GATEUP>(g, waves, stream); return true;
+    case 1 * 16 + 4: *err = launch_ws2<1, 4, GATEUP>(g, waves, stream); return true;
+    case 1 * 16 + 8: *err = launch_ws2<1, 8, GATEUP>(g, waves, stream); return true;
+    case 2 * 16 + 4: *err = launch_ws2<2, 4, GATEUP>(g, waves, stream); return true;
+    case 2 * 16 + 8: *err = launch_ws2<2, 8, GATEUP>(g, waves, stream); return true;
+    case 4 * 16 + 8: *err = launch_ws2<4, 8, GATEUP>(g, waves, stream); return true;
+    default: return false;
+  }
+}
 
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
-                          const ExpertWeights &w, float *h, int32_t msub, int32_t waves,
-                          int32_t nb, hipStream_t stream) {
+                          const ExpertWeights &w, float *h, int32_t msub, int32_t msub_big,
+                          int32_t waves, int32_t nb, hipStream_t stream) {
   GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
+  hipError_t err;
+  if (nb == 2 && launch_pair<true>(g, msub, msub_big, waves, stream, &err)) return err;
   if (msub >= 16) return launch_ws<16, 2, true>(g, waves, stream);
   if (nb >= 4) {
     if (msub >= 8) return launch_ws<8, 4, true>(g, waves, stream);
@@ -224,8 +278,8 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
 }
 
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
-                       const ExpertWeights &w, float *y, int32_t msub, int32_t splits,
-                       int32_t waves, int32_t nb, hipStream_t stream) {
+                       const ExpertWeights &w, float *y, int32_t msub, int32_t msub_big,
+                       int32_t splits, int32_t waves, int32_t nb, hipStream_t stream) {
   if (h32) {
     GemmArgs g{rs, nullptr, nullptr, h32, w, y, 1, rs.f};
     const int blocks = grid_items(rs) * ((rs.d + 63) >> 6);
@@ -236,6 +290,9 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   int32_t ksplit;
   down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
+  // ksplit is a whole number of msub chunks, hence of msub_big chunks too
+  hipError_t err;
+  if (nb == 2 && launch_pair<false>(g, msub, msub_big, waves, stream, &err)) return err;
   if (msub >= 16) return launch_ws<16, 2, false>(g, waves, stream);
   if (nb >= 4) {
     if (msub >= 8) return launch_ws<8, 4, false>(g, waves, stream);

@@ -28,16 +28,20 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_count_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int b0, b1;
   slice_range(P, blockIdx.x, b0, b1);
-  for (int i = tid; i < kSliceWaves * E; i += kSliceWaves * kWave) cnt[i] = 0;
-  __syncthreads();
   const int per = (b1 - b0 + kSliceWaves - 1) / kSliceWaves;
   const int w0 = min(b1, b0 + wave * per), w1 = min(b1, w0 + per);
+  for (int e = lane; e < E; e += kWave) cnt[wave * E + e] = 0;  // this wave's row
+  __builtin_amdgcn_wave_barrier();
   slice_count(ids, w0, w1, expert_bits(E), cnt + wave * E, lane);
   __syncthreads();
   for (int e = tid; e < E; e += kSliceWaves * kWave) {
-    int c = 0;
-    for (int w = 0; w < kSliceWaves; ++w) c += cnt[w * E + e];
-    inv_pairs[b0 + e] = c;  // this slice's count of expert e
+    int c[kSliceWaves];
+#pragma unroll
+    for (int w = 0; w < kSliceWaves; ++w) c[w] = cnt[w * E + e];
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kSliceWaves; ++w) t += c[w];
+    inv_pairs[b0 + e] = t;  // this slice's count of expert e
   }
 }
 
@@ -72,19 +76,23 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_scatter_kernel(
   int b0, b1;
   slice_range(P, blockIdx.x, b0, b1);
   for (int e = tid; e < E; e += kSliceWaves * kWave) base[e] = inv_pairs[b0 + e];
-  for (int i = tid; i < kSliceWaves * E; i += kSliceWaves * kWave) cnt[i] = 0;
-  __syncthreads();  // the slice's bases are read before its inv_pairs entries are written
   const int per = (b1 - b0 + kSliceWaves - 1) / kSliceWaves;
   const int w0 = min(b1, b0 + wave * per), w1 = min(b1, w0 + per);
   const int nbits = expert_bits(E);
+  for (int e = lane; e < E; e += kWave) cnt[wave * E + e] = 0;  // this wave's row
+  __builtin_amdgcn_wave_barrier();
   slice_count(ids, w0, w1, nbits, cnt + wave * E, lane);
+  // the slice's bases are read (above) before its inv_pairs entries are written (scatter)
   __syncthreads();
   for (int e = tid; e < E; e += kSliceWaves * kWave) {
+    int c[kSliceWaves];
+#pragma unroll
+    for (int w = 0; w < kSliceWaves; ++w) c[w] = cnt[w * E + e];
     int s = base[e];
+#pragma unroll
     for (int w = 0; w < kSliceWaves; ++w) {
-      const int c = cnt[w * E + e];
       cnt[w * E + e] = s;
-      s += c;
+      s += c[w];
     }
   }
   __syncthreads();

@@ -29,15 +29,6 @@ constexpr int permute_lds_ints() {
   return NW * kMaxExperts + kMaxExperts + 2 * (kMaxExperts + 1);
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
 // Lanes (among `valid` ones) holding the same expert id as this lane.
 __device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int nbits) {
   uint64_t m = __ballot(valid);
@@ -63,6 +54,7 @@ __device__ __forceinline__ void slice_count(const int32_t *__restrict__ ids, int
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
+      if (base + u * kWave >= b1) break;  // uniform: the rest of the batch is past the slice
       const int e = ev[u];
       const bool valid = e >= 0;
       const uint64_t m = same_expert_mask(e, valid, nbits);
@@ -87,6 +79,7 @@ __device__ __forceinline__ void slice_scatter(const int32_t *__restrict__ ids, i
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
+      if (base + u * kWave >= b1) break;  // uniform
       const int p = base + u * kWave + lane;
       const int e = ev[u];
       const bool valid = e >= 0;
@@ -129,25 +122,37 @@ __device__ __forceinline__ void build_layout(const int *tot, int *off, int *item
                                              int S) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sentinel = P;
-  // exclusive scan of padded totals; work-list offsets
+  // exclusive scan of padded totals and of work-list offsets: lane l holds
+  // experts [l*per, (l+1)*per), summed locally, then one wave scan
   if (wave == 0) {
-    int run = 0, irun = 0;
-    for (int base = 0; base < E; base += kWave) {
-      const int e = base + lane;
-      const int pad = e < E ? (tot[e] + bm - 1) / bm * bm : 0;
-      const int inc = wave_incl_scan(pad, lane);
-      const int ni = (e < E && row_chunk > 0) ? (pad + row_chunk - 1) / row_chunk : 0;
-      const int iinc = wave_incl_scan(ni, lane);
-      if (e < E) {
-        off[e] = run + inc - pad;
-        item_off[e] = irun + iinc - ni;
-      }
-      run += __shfl(inc, kWave - 1, kWave);
-      irun += __shfl(iinc, kWave - 1, kWave);
+    constexpr int PER = kMaxExperts / kWave;
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = lane * per;
+    int pad[PER], ni[PER], ps = 0, is = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = e0 + j;
+      const bool v = j < per && e < E;
+      pad[j] = v ? (tot[e] + bm - 1) / bm * bm : 0;
+      ni[j] = (v && row_chunk > 0) ? (pad[j] + row_chunk - 1) / row_chunk : 0;
+      ps += pad[j];
+      is += ni[j];
     }
-    if (lane == 0) {
-      off[E] = run;
-      item_off[E] = irun;
+    const int pinc = wave_incl_scan(ps, lane), iinc = wave_incl_scan(is, lane);
+    int run = pinc - ps, irun = iinc - is;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = e0 + j;
+      if (j < per && e < E) {
+        off[e] = run;
+        item_off[e] = irun;
+      }
+      run += pad[j];
+      irun += ni[j];
+    }
+    if (lane == kWave - 1) {
+      off[E] = pinc;
+      item_off[E] = iinc;
     }
   }
   __syncthreads();
@@ -201,22 +206,25 @@ __device__ __forceinline__ void permute_block(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nbits = expert_bits(E);
 
-  for (int i = tid; i < NW * E; i += NT) cnt[i] = 0;
-  __syncthreads();
-
-  const int per = (P + NW - 1) / NW;
+  // slices are whole 64-pair steps, so short batches leave the last waves idle
+  const int per = (P + NW * kWave - 1) / (NW * kWave) * kWave;
   const int b0 = min(P, wave * per), b1 = min(P, b0 + per);
   int *my = cnt + wave * E;
+  for (int e = lane; e < E; e += kWave) my[e] = 0;  // only this wave uses its row until the barrier
+  __builtin_amdgcn_wave_barrier();
   slice_count(ids, b0, b1, nbits, my, lane);
   __syncthreads();
 
-  // exclusive prefix over waves per expert; totals
+  // exclusive prefix over waves per expert (all NW counts read first); totals
   for (int e = tid; e < E; e += NT) {
+    int c[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c[w] = cnt[w * E + e];
     int s = 0;
+#pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w * E + e];
       cnt[w * E + e] = s;
-      s += c;
+      s += c[w];
     }
     tot[e] = s;
   }

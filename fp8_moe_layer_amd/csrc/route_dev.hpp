@@ -161,6 +161,13 @@ __device__ __forceinline__ uint64_t route_key(float l, int e) {
   return ((uint64_t)ord << 32) | (uint32_t)(0xFFFF - e);
 }
 
+// The logit a key was made from (-0 comes back as +0, which gives the same
+// exponentials below).
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
 constexpr int kTopkSlots = kMaxExperts / kWave;
 
 // l: the token's E logits (global memory or LDS); writes the token's k_max
@@ -168,11 +175,18 @@ constexpr int kTopkSlots = kMaxExperts / kWave;
 __device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, int kt,
                                               int32_t *__restrict__ ids_row,
                                               float *__restrict__ w_row, int lane) {
+  // every slot's logit is requested before any is used (one memory latency)
+  float lv[kTopkSlots];
+#pragma unroll
+  for (int c = 0; c < kTopkSlots; ++c) {
+    const int e = lane + c * kWave;
+    lv[c] = c * kWave < E ? l[e < E ? e : E - 1] : 0.0f;
+  }
   uint64_t key[kTopkSlots];
 #pragma unroll
   for (int c = 0; c < kTopkSlots; ++c) {
-    int e = lane + c * kWave;
-    key[c] = e < E ? route_key(l[e], e) : 0ull;
+    const int e = lane + c * kWave;
+    key[c] = e < E ? route_key(lv[c], e) : 0ull;
   }
   float m = 0.0f, z = 0.0f, my_eps = 0.0f;
   int my_id = -1;
@@ -182,7 +196,7 @@ __device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, 
     for (int c = 0; c < kTopkSlots; ++c) best = key[c] > best ? key[c] : best;
     best = wave_max_u64(best);
     const int e = 0xFFFF - (int)(best & 0xFFFFu);
-    const float lv = l[e];
+    const float lv = key_logit(best);  // no dependent memory read per round
     if (j == 0) m = lv;
     const float eps = expf(lv - m);
     z += eps;

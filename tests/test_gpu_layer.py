@@ -153,6 +153,18 @@ def test_gemm_geometry_overrides(small, msub, waves, nb, monkeypatch):
     _check(small, no_requant=True)
 
 
+@pytest.mark.parametrize("ms,ml", [(1, 2), (1, 4), (1, 8), (2, 4), (2, 8), (4, 8)])
+def test_two_shape_gemm(small, ms, ml, monkeypatch):
+    """Work items cut at 16*ml rows, the ones of at most 16*ms rows on the
+    short row-pass shape and the rest on the long one, in one launch: the
+    same parity on every token."""
+    monkeypatch.setenv("FP8MOE_MSUB", str(ms))
+    monkeypatch.setenv("FP8MOE_MSUB_BIG", str(ml))
+    _check(small)
+    _check(small, no_requant=True)
+    _check(small, block_m=32)
+
+
 def test_persistent_flag_is_refused(small):
     for nr in (False, True):
         with pytest.raises(lib().MoEError):
