@@ -82,6 +82,19 @@ __device__ __forceinline__ bool row_real(const RowSpace &rs, int grow) {
   return grow >= rs.capacity || rs.sorted_pairs[grow] < rs.T * rs.k_max;
 }
 
+// Activation row read for expert row `grow` of a GEMM (the token for gate/up,
+// the expert row itself for down), or -1 for a padding row or !ok.  sp is
+// sorted_pairs[min(grow, capacity - 1)], loaded by the caller.  Branch-free,
+// so that the caller's loads are not sunk into branches and stay together.
+template <bool GATEUP>
+__device__ __forceinline__ int act_row(const RowSpace &rs, int grow, int sp, bool ok) {
+  const bool sh_row = grow >= rs.capacity;
+  const bool real = sh_row | (sp < rs.T * rs.k_max);
+  int a = grow;
+  if (GATEUP) a = sh_row ? (grow - rs.capacity) % rs.T : sp / rs.k_max;
+  return (ok & real) ? a : -1;
+}
+
 // LDS-only workgroup barrier: waits for this wave's LDS operations, not for
 // its outstanding global loads.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -91,7 +104,6 @@ __device__ __forceinline__ void barrier_after_loads() {
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr;
-
 
 // 64 zero bytes: the source of activation pieces for padding rows and K
 // past the end.  Never written (each translation unit has its own copy).
@@ -112,9 +124,8 @@ struct Chunk {
   static constexpr int PF = MSUB <= 2 ? 4 : 2;
   // LDS: the activation ring, then a table of the activation scale of each
   // row of the current pass (two copies by pass parity), 0 for a padding
-  // row.  The loader waves fill the table with the same row lookups they
-  // make for the gather, so the epilogue needs no global loads on its
-  // critical path.
+  // row.  The compute waves fill it while their first weight loads are in
+  // flight, so the epilogue needs no global loads on its critical path.
   static constexpr int RING = NBUF * BYTES;
   static constexpr int LDS = RING + 2 * MP * (int)sizeof(float);
 };
@@ -191,30 +202,45 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
     for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
       const int prow = min(C::MP, rows - p0);
       const int msub = (prow + 15) >> 4;
-      float *rsc = row_scale + (pass & 1) * C::MP;
+      // The row lookups of all the loader's row groups, and of its share of
+      // the pass's scale table (rows tfirst + 64*t + lane of the pass), are
+      // issued together (unconditional loads at clamped indices), so a
+      // pass's gather starts after one memory latency, not one or two per
+      // row group.
+      constexpr int TB = (C::MP / kWave + C::LOADERS - 1) / C::LOADERS;
+      constexpr int TBn = TB > 0 ? TB : 1;  // table blocks of 64 rows per loader
+      const int tfirst = (wave - W) * TBn * kWave;
+      int grow[C::MPL], sp[C::MPL], tgrow[TBn], tsp[TBn];
 #pragma unroll
       for (int mm = 0; mm < C::MPL; ++mm) {
-        const int m = mbase + mm;
-        const int r = p0 + m * 16 + ln;
-        const uint8_t *b = nullptr;
-        float sc = 0.0f;
-        if (m < msub && r < rows) {
-          if (GATEUP) {
-            const int tok = row_token(rs, row0 + r);
-            if (tok >= 0) {
-              b = g.a + (size_t)tok * K;
-              sc = g.a_scale[tok];
-            }
-          } else if (row_real(rs, row0 + r)) {
-            b = g.a + (size_t)(row0 + r) * K;
-            sc = g.a_scale[row0 + r];
-          }
-        }
-        abase[mm] = b;
-        if (kg == 0) rsc[m * 16 + ln] = sc;
+        grow[mm] = row0 + min(p0 + (mbase + mm) * 16 + ln, rows - 1);
+        sp[mm] = rs.sorted_pairs[min(grow[mm], rs.capacity - 1)];
       }
-      // the table is complete before the first barrier of the pass
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < TBn; ++t) {
+        tgrow[t] = row0 + min(p0 + tfirst + t * kWave + lane, rows - 1);
+        tsp[t] = rs.sorted_pairs[min(tgrow[t], rs.capacity - 1)];
+      }
+#pragma unroll
+      for (int mm = 0; mm < C::MPL; ++mm) {
+        const int r = p0 + (mbase + mm) * 16 + ln;
+        const int a = act_row<GATEUP>(rs, grow[mm], sp[mm], mbase + mm < msub && r < rows);
+        abase[mm] = a < 0 ? nullptr : g.a + (size_t)a * K;
+      }
+      const float *tsrc[TBn];
+#pragma unroll
+      for (int t = 0; t < TBn; ++t) {
+        const int a = act_row<GATEUP>(rs, tgrow[t], tsp[t], tfirst + t * kWave + lane < prow);
+        tsrc[t] = a < 0 ? reinterpret_cast<const float *>(g_zero_piece) : g.a_scale + a;
+      }
+      // The table goes to LDS by direct-to-LDS dword loads (a padding row
+      // loads a zero) issued before chunk 0's, so the wait for chunk 0 also
+      // covers them; lanes past the table stay idle.
+      float *rsc = row_scale + (pass & 1) * C::MP;
+#pragma unroll
+      for (int t = 0; t < TBn; ++t)
+        if (tfirst + t * kWave + lane < C::MP)
+          __builtin_amdgcn_global_load_lds(tsrc[t], (lds_ptr)(rsc + tfirst + t * kWave), 4, 0, 0);
       auto issue = [&](int c) {
         uint8_t *dst = abuf + (c % C::NBUF) * C::BYTES;
 #pragma unroll
