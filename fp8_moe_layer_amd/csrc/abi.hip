@@ -135,6 +135,19 @@ int32_t choose_msub_big(const moe_dims *d, int32_t msub) {
   return m;
 }
 
+// Non-temporal weight loads pay off where each weight byte is read by one
+// workgroup (every expert's rows, routed and shared, expected in one work
+// item) over a long enough K range (measured: K >= 2048 bytes gains, short
+// ranges and weights re-read by several items lose).
+bool stream_weights(const moe_dims *d, int32_t msub_big, int32_t kbytes) {
+  const int forced = env_int("FP8MOE_NT", -1);  // tile-tuning override
+  if (forced == 0 || forced == 1) return forced == 1;
+  const double mean = (double)d->T * d->k_max / d->E;
+  const double est = mean + 4.0 * sqrt(mean) + 2.0;
+  const int64_t chunk = 16 * (int64_t)msub_big;
+  return est <= chunk && (d->n_shared == 0 || d->T <= chunk) && kbytes >= 2048;
+}
+
 // Expected work items of the grouped GEMMs (rows cut into 16*msub chunks).
 double expected_items(const moe_dims *d, int32_t msub) {
   const double chunk = 16.0 * msub;
@@ -211,6 +224,7 @@ struct Layout {
   size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
       hq, sh, y, total;
   int32_t capacity, rows_total, max_items, row_chunk, msub, msub_big, splits;
+  bool nt_gu, nt_dn;  // non-temporal weight loads
   GemmPlan gu, dn;
 };
 
@@ -226,6 +240,13 @@ Layout layout_of(const moe_dims *d) {
   L.msub_big = (L.gu.nb == 2 && L.dn.nb == 2) ? choose_msub_big(d, L.msub) : L.msub;
   L.row_chunk = 16 * L.msub_big;
   L.splits = L.dn.splits;
+  {
+    int32_t sp, ks;
+    down_split_geometry(d->f, L.msub, L.splits, &sp, &ks);
+    L.nt_gu = L.gu.nb == 2 && L.msub <= 8 && stream_weights(d, L.msub_big, d->d);
+    L.nt_dn = L.dn.nb == 2 && L.msub <= 8 && !(d->flags & MOE_F_NO_REQUANT) &&
+              stream_weights(d, L.msub_big, ks);
+  }
   L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
   const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
   size_t o = 0;
@@ -412,8 +433,9 @@ moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
   const int32_t msub = choose_msub(dims);
   const GemmPlan gp = plan_gemm(dims, msub, true);
-  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub,
-                                gp.nb == 2 ? choose_msub_big(dims, msub) : msub, gp.waves, gp.nb,
+  const int32_t mbig = gp.nb == 2 ? choose_msub_big(dims, msub) : msub;
+  const bool nt = gp.nb == 2 && msub <= 8 && stream_weights(dims, mbig, dims->d);
+  s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub, mbig, gp.waves, gp.nb, nt,
                                 as_stream(stream)),
                  fn);
   return s ? s : ok();
@@ -435,9 +457,12 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
   RowSpace rs = row_space(dims, capacity, sorted_pairs, expert_offsets);
   const int32_t msub = choose_msub(dims);
   const GemmPlan dp = plan_gemm(dims, msub, false);
+  const int32_t mbig = dp.nb == 2 ? choose_msub_big(dims, msub) : msub;
+  int32_t sp, ks;
+  down_split_geometry(dims->f, msub, 1, &sp, &ks);
+  const bool nt = !f32 && dp.nb == 2 && msub <= 8 && stream_weights(dims, mbig, ks);
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
-                             msub, dp.nb == 2 ? choose_msub_big(dims, msub) : msub, 1, dp.waves,
-                             dp.nb, as_stream(stream)),
+                             msub, mbig, 1, dp.waves, dp.nb, nt, as_stream(stream)),
                  fn);
   return s ? s : ok();
 }
@@ -551,17 +576,17 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
   rs.max_items = L.max_items;
   const ExpertWeights ew = to_internal(w);
   mark(3);
-  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, st), "gate_up"))) return s;
+  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, L.nt_gu, st), "gate_up"))) return s;
   mark(4);
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, st),
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
                         "down")))
       return s;
   } else {
     mark(5);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, st), "down")))
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, false, st), "down")))
       return s;
   }
   mark(6);

@@ -156,7 +156,9 @@ __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
 // the loader wave(s); the tile is W * (GATEUP ? 8 : 16) * NB output channels
 // wide.  abuf: Chunk<MSUB>::LDS bytes of LDS, 1024-byte aligned.  Returns
 // early (uniformly) for an empty item.
-template <int MSUB, int NB, bool GATEUP>
+// NT: the weight loads carry the non-temporal hint, so that a weight stream
+// read once does not push the activation rows and row tables out of L2.
+template <int MSUB, int NB, bool GATEUP, bool NT = false>
 __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t *abuf) {
   using C = Chunk<MSUB>;
   static_assert(C::LPC == 16 && C::NBUF == 4, "loader_wait_barrier assumes 16 loads per chunk");
@@ -300,8 +302,8 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
     const int o1 = o0 + 1024;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const v4i lo = load16(bw[nb] + o0);
-      const v4i hi = load16(bw[nb] + o1);
+      const v4i lo = NT ? load16_nt(bw[nb] + o0) : load16(bw[nb] + o0);
+      const v4i hi = NT ? load16_nt(bw[nb] + o1) : load16(bw[nb] + o1);
       b[nb] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
   };

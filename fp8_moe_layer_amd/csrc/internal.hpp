@@ -77,9 +77,11 @@ constexpr int kGemmMaxThreadsWide = 8 * 64;
 constexpr int kGemmMaxWaves16 = 6;
 // msub_big > msub (nb 2, msub_big <= 8): items longer than 16*msub rows run
 // 16*msub_big-row passes in the same launch (items are cut at 16*msub_big).
+// stream_weights (nb 2, msub <= 8): the weight loads carry the non-temporal
+// hint -- for weights that one workgroup each reads once.
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t msub_big,
-                          int32_t waves, int32_t nb, hipStream_t stream);
+                          int32_t waves, int32_t nb, bool stream_weights, hipStream_t stream);
 // Per-row e4m3 requantisation of h (real rows only): hq codes, sh = amax/448.
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream);
@@ -89,7 +91,8 @@ hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float
 // count actually used is down_splits_used(f, msub, splits).
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t msub_big,
-                       int32_t splits, int32_t waves, int32_t nb, hipStream_t stream);
+                       int32_t splits, int32_t waves, int32_t nb, bool stream_weights,
+                       hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
 // Final K-split count and bytes per split for a requested split count.
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,

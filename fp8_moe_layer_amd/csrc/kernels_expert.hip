@@ -41,11 +41,11 @@ namespace fp8moe {
 // W compute waves + the loader wave(s).  With up to five compute waves and
 // row passes of up to 128 rows two workgroups share a CU; otherwise one
 // workgroup per CU (256-row passes use 130 KB of LDS and up to 256 VGPRs).
-template <int MSUB, int NB, bool GATEUP>
+template <int MSUB, int NB, bool GATEUP, bool NT>
 __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMaxThreads) void wsgemm_kernel(
     GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t abuf[Chunk<MSUB>::LDS];
-  wsgemm_tile<MSUB, NB, GATEUP>(g, blockIdx.x, abuf);
+  wsgemm_tile<MSUB, NB, GATEUP, NT>(g, blockIdx.x, abuf);
 }
 
 // Two row-pass shapes in one launch.  Work items are cut at 16*ML rows; an
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMax
 // of their weights once, and the common short items keep the faster shape.
 // Both shapes have one loader wave and two weight operands per wave, hence
 // the same tiling of the grid.
-template <int MS, int ML, bool GATEUP>
+template <int MS, int ML, bool GATEUP, bool NT>
 __global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
   static_assert(MS < ML && Chunk<ML>::LOADERS == 1, "two row-pass shapes, one loader wave");
   constexpr int LDS = Chunk<ML>::LDS > Chunk<MS>::LDS ? Chunk<ML>::LDS : Chunk<MS>::LDS;
@@ -68,9 +68,9 @@ __global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
   int expert, row0, rows;
   if (!resolve_item(g.rs, item_id, expert, row0, rows)) return;
   if (__builtin_amdgcn_readfirstlane(rows) <= 16 * MS)
-    wsgemm_tile<MS, 2, GATEUP>(g, blockIdx.x, abuf);
+    wsgemm_tile<MS, 2, GATEUP, NT>(g, blockIdx.x, abuf);
   else
-    wsgemm_tile<ML, 2, GATEUP>(g, blockIdx.x, abuf);
+    wsgemm_tile<ML, 2, GATEUP, NT>(g, blockIdx.x, abuf);
 }
 
 // ------------------------------------------------------------------ down, fp32 products
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *
 
 static int grid_items(const RowSpace &rs) { return rs.items ? rs.max_items : rs.E + rs.S; }
 
-template <int MSUB, int NB, bool GATEUP>
+template <int MSUB, int NB, bool GATEUP, bool NT = false>
 static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
   const int N = GATEUP ? g.rs.f : g.rs.d;
   const int ch_wave = GATEUP ? 8 * NB : 16 * NB;
@@ -192,11 +192,11 @@ static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
   const int n_tiles = (N + wv * ch_wave - 1) / (wv * ch_wave);
   const int blocks = grid_items(g.rs) * n_tiles * g.splits;
   if (blocks == 0) return hipSuccess;
-  wsgemm_kernel<MSUB, NB, GATEUP><<<blocks, (wv + Chunk<MSUB>::LOADERS) * 64, 0, stream>>>(g);
+  wsgemm_kernel<MSUB, NB, GATEUP, NT><<<blocks, (wv + Chunk<MSUB>::LOADERS) * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 
-template <int MS, int ML, bool GATEUP>
+template <int MS, int ML, bool GATEUP, bool NT>
 static hipError_t launch_ws2(const GemmArgs &g, int waves, hipStream_t stream) {
   const int N = GATEUP ? g.rs.f : g.rs.d;
   const int ch_wave = GATEUP ? 16 : 32;
@@ -204,31 +204,42 @@ static hipError_t launch_ws2(const GemmArgs &g, int waves, hipStream_t stream) {
   const int n_tiles = (N + wv * ch_wave - 1) / (wv * ch_wave);
   const int blocks = grid_items(g.rs) * n_tiles * g.splits;
   if (blocks == 0) return hipSuccess;
-  wsgemm2_kernel<MS, ML, GATEUP><<<blocks, (wv + 1) * 64, 0, stream>>>(g);
+  wsgemm2_kernel<MS, ML, GATEUP, NT><<<blocks, (wv + 1) * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 
 // The two-shape kernel for (msub, msub_big), or false when that pair has none.
-template <bool GATEUP>
+template <bool GATEUP, bool NT>
 static bool launch_pair(const GemmArgs &g, int msub, int msub_big, int waves, hipStream_t stream,
                         hipError_t *err) {
   switch (msub * 16 + msub_big) {
-    case 1 * 16 + 2: *err = launch_ws2<1, 2, GATEUP>(g, waves, stream); return true;
-    case 1 * 16 + 4: *err = launch_ws2<1, 4, GATEUP>(g, waves, stream); return true;
-    case 1 * 16 + 8: *err = launch_ws2<1, 8, GATEUP>(g, waves, stream); return true;
-    case 2 * 16 + 4: *err = launch_ws2<2, 4, GATEUP>(g, waves, stream); return true;
-    case 2 * 16 + 8: *err = launch_ws2<2, 8, GATEUP>(g, waves, stream); return true;
-    case 4 * 16 + 8: *err = launch_ws2<4, 8, GATEUP>(g, waves, stream); return true;
+    case 1 * 16 + 2: *err = launch_ws2<1, 2, GATEUP, NT>(g, waves, stream); return true;
+    case 1 * 16 + 4: *err = launch_ws2<1, 4, GATEUP, NT>(g, waves, stream); return true;
+    case 1 * 16 + 8: *err = launch_ws2<1, 8, GATEUP, NT>(g, waves, stream); return true;
+    case 2 * 16 + 4: *err = launch_ws2<2, 4, GATEUP, NT>(g, waves, stream); return true;
+    case 2 * 16 + 8: *err = launch_ws2<2, 8, GATEUP, NT>(g, waves, stream); return true;
+    case 4 * 16 + 8: *err = launch_ws2<4, 8, GATEUP, NT>(g, waves, stream); return true;
     default: return false;
   }
 }
 
+// Row passes of up to 128 rows with two weight operands per wave, with or
+// without the non-temporal weight hint.
+template <bool GATEUP, bool NT>
+static hipError_t launch_nb2(const GemmArgs &g, int msub, int msub_big, int waves,
+                             hipStream_t stream) {
+  hipError_t err;
+  if (launch_pair<GATEUP, NT>(g, msub, msub_big, waves, stream, &err)) return err;
+  if (msub >= 8) return launch_ws<8, 2, GATEUP, NT>(g, waves, stream);
+  if (msub >= 4) return launch_ws<4, 2, GATEUP, NT>(g, waves, stream);
+  if (msub >= 2) return launch_ws<2, 2, GATEUP, NT>(g, waves, stream);
+  return launch_ws<1, 2, GATEUP, NT>(g, waves, stream);
+}
+
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t msub_big,
-                          int32_t waves, int32_t nb, hipStream_t stream) {
+                          int32_t waves, int32_t nb, bool stream_weights, hipStream_t stream) {
   GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
-  hipError_t err;
-  if (nb == 2 && launch_pair<true>(g, msub, msub_big, waves, stream, &err)) return err;
   if (msub >= 16) return launch_ws<16, 2, true>(g, waves, stream);
   if (nb >= 4) {
     if (msub >= 8) return launch_ws<8, 4, true>(g, waves, stream);
@@ -236,10 +247,8 @@ hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx
     if (msub >= 2) return launch_ws<2, 4, true>(g, waves, stream);
     return launch_ws<1, 4, true>(g, waves, stream);
   }
-  if (msub >= 8) return launch_ws<8, 2, true>(g, waves, stream);
-  if (msub >= 4) return launch_ws<4, 2, true>(g, waves, stream);
-  if (msub >= 2) return launch_ws<2, 2, true>(g, waves, stream);
-  return launch_ws<1, 2, true>(g, waves, stream);
+  return stream_weights ? launch_nb2<true, true>(g, msub, msub_big, waves, stream)
+                        : launch_nb2<true, false>(g, msub, msub_big, waves, stream);
 }
 
 // Rows of up to 4096 values: a wave per row, four rows per workgroup.
@@ -279,7 +288,8 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
 
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
                        const ExpertWeights &w, float *y, int32_t msub, int32_t msub_big,
-                       int32_t splits, int32_t waves, int32_t nb, hipStream_t stream) {
+                       int32_t splits, int32_t waves, int32_t nb, bool stream_weights,
+                       hipStream_t stream) {
   if (h32) {
     GemmArgs g{rs, nullptr, nullptr, h32, w, y, 1, rs.f};
     const int blocks = grid_items(rs) * ((rs.d + 63) >> 6);
@@ -291,8 +301,6 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
   // ksplit is a whole number of msub chunks, hence of msub_big chunks too
-  hipError_t err;
-  if (nb == 2 && launch_pair<false>(g, msub, msub_big, waves, stream, &err)) return err;
   if (msub >= 16) return launch_ws<16, 2, false>(g, waves, stream);
   if (nb >= 4) {
     if (msub >= 8) return launch_ws<8, 4, false>(g, waves, stream);
@@ -300,10 +308,8 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
     if (msub >= 2) return launch_ws<2, 4, false>(g, waves, stream);
     return launch_ws<1, 4, false>(g, waves, stream);
   }
-  if (msub >= 8) return launch_ws<8, 2, false>(g, waves, stream);
-  if (msub >= 4) return launch_ws<4, 2, false>(g, waves, stream);
-  if (msub >= 2) return launch_ws<2, 2, false>(g, waves, stream);
-  return launch_ws<1, 2, false>(g, waves, stream);
+  return stream_weights ? launch_nb2<false, true>(g, msub, msub_big, waves, stream)
+                        : launch_nb2<false, false>(g, msub, msub_big, waves, stream);
 }
 
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,

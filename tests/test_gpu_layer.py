@@ -165,6 +165,15 @@ def test_two_shape_gemm(small, ms, ml, monkeypatch):
     _check(small, block_m=32)
 
 
+@pytest.mark.parametrize("nt", [0, 1])
+def test_streamed_weight_loads(small, nt, monkeypatch):
+    """The grouped GEMMs with and without the non-temporal weight-load hint
+    give the same parity on every token."""
+    monkeypatch.setenv("FP8MOE_NT", str(nt))
+    _check(small)
+    _check(small, no_requant=True)
+
+
 def test_persistent_flag_is_refused(small):
     for nr in (False, True):
         with pytest.raises(lib().MoEError):
