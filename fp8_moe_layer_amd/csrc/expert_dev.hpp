@@ -364,7 +364,10 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
                 const float sxt = rsc[m * 16 + kg * 4 + i];
                 const float gv = acc[m][2 * cg][i] * sxt * sgo;
                 const float uv = acc[m][2 * cg + 1][i] * sxt * suo;
-                g.out[(size_t)(row0 + r) * N + o] = gv / (1.0f + expf(-gv)) * uv;
+                // non-temporal: the store stream does not push the weight
+                // stream's neighbours (activation rows, tables) out of L2
+                __builtin_nontemporal_store(gv / (1.0f + expf(-gv)) * uv,
+                                            &g.out[(size_t)(row0 + r) * N + o]);
               }
             }
           }
@@ -388,7 +391,9 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
               const int grow = row0 + r;
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) {
-                if (ch[nb] < N) ys[(size_t)grow * N + ch[nb]] = acc[m][nb][i] * shr * sdv[nb];
+                if (ch[nb] < N)  // non-temporal, as h above
+                  __builtin_nontemporal_store(acc[m][nb][i] * shr * sdv[nb],
+                                              &ys[(size_t)grow * N + ch[nb]]);
               }
             }
           }
