@@ -200,9 +200,9 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
       const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);
       const double rate = std::min(1.0, W * per_cu * nb / 12.0);
       int last = 0;
-      for (int want = 1; want <= (can_split ? 8 : 1); ++want) {
-        const int sp =
-            can_split ? down_splits_used(d->f, msub, forced_splits > 0 ? forced_splits : want) : 1;
+      for (int want = 1; want <= (can_split ? kMaxDownSplits : 1); ++want) {
+        const int req = forced_splits > 0 ? std::min(forced_splits, kMaxDownSplits) : want;
+        const int sp = can_split ? down_splits_used(d->f, msub, req) : 1;
         if (sp == last) continue;
         last = sp;
         const double n = items * tiles * sp;

@@ -454,45 +454,69 @@ __device__ __forceinline__ void requant_row_wave(const RowSpace &rs, const float
 // shared experts' rows in order; each y row is the sum of its K-split slabs
 // in split order.  A workgroup of NT threads does NT*4 columns of token t
 // starting at column c0.
+//
+// Slots are taken G at a time: their lookups (ids, inv, w) are requested
+// together, then every K-split piece of their rows (up to SM splits), then
+// the pieces are added in order -- two memory latencies per group.
+template <int G, int SM>
+__device__ __forceinline__ v4f combine_groups(const RowSpace &rs, const float *__restrict__ y,
+                                              int splits, const int32_t *__restrict__ ids,
+                                              const float *__restrict__ w,
+                                              const int32_t *__restrict__ inv, int t, int c) {
+  const int d = rs.d, K = rs.k_max, J = K + rs.S;  // routed slots, then the shared rows
+  const size_t slab = (size_t)(rs.capacity + rs.S * rs.T) * d;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < J; j0 += G) {
+    int row[G];
+    float wt[G];
+    bool ok[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = j0 + u;
+      if (j < K) {
+        const int p = t * K + j;
+        const int id = ids[p], r = inv[p];
+        wt[u] = w[p];
+        ok[u] = id >= 0;
+        row[u] = id >= 0 ? r : 0;
+      } else {  // a shared row (weight 1: 1 * x == x), or past the end
+        wt[u] = 1.0f;
+        ok[u] = j < J;
+        row[u] = j < J ? rs.capacity + (j - K) * rs.T + t : 0;
+      }
+    }
+    v4f v[G][SM];
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+      for (int sp = 0; sp < SM; ++sp)  // uniform conditions
+        if (j0 + u < J && sp < splits)
+          v[u][sp] = *reinterpret_cast<const v4f *>(y + sp * slab + (size_t)row[u] * d + c);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (j0 + u < J) {
+        v4f cur = v[u][0];
+#pragma unroll
+        for (int sp = 1; sp < SM; ++sp)
+          if (sp < splits) cur += v[u][sp];
+        if (ok[u]) acc += wt[u] * cur;
+      }
+    }
+  }
+  return acc;
+}
+
 template <int NT>
 __device__ __forceinline__ void combine_chunk(const RowSpace &rs, const float *__restrict__ y,
                                               int splits, const int32_t *__restrict__ ids,
                                               const float *__restrict__ w,
                                               const int32_t *__restrict__ inv,
                                               float *__restrict__ out, int t, int c0) {
-  const int d = rs.d, K = rs.k_max;
-  const size_t slab = (size_t)(rs.capacity + rs.S * rs.T) * d;
   const int c = c0 + threadIdx.x * 4;
-  if (c >= d) return;
-  auto yrow = [&](size_t row) {
-    v4f v = *reinterpret_cast<const v4f *>(y + row * d + c);
-    for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const v4f *>(y + s * slab + row * d + c);
-    return v;
-  };
-  // slots in groups of 8: all their rows are fetched before any is added,
-  // and the sum still runs in slot order
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int G = 8;
-  for (int j0 = 0; j0 < K; j0 += G) {
-    int row[G];
-    float wt[G];
-    v4f yv[G];
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const int j = j0 + u, p = t * K + j;
-      const bool ok = j < K && ids[p] >= 0;
-      row[u] = ok ? inv[p] : -1;
-      wt[u] = ok ? w[p] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-      if (row[u] >= 0) yv[u] = yrow((size_t)row[u]);
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-      if (row[u] >= 0) acc += wt[u] * yv[u];
-  }
-  for (int s = 0; s < rs.S; ++s) acc += yrow((size_t)rs.capacity + (size_t)s * rs.T + t);
-  *reinterpret_cast<v4f *>(out + (size_t)t * d + c) = acc;
+  if (c >= rs.d) return;
+  const v4f acc = splits <= 2 ? combine_groups<8, 2>(rs, y, splits, ids, w, inv, t, c)
+                              : combine_groups<2, kMaxDownSplits>(rs, y, splits, ids, w, inv, t, c);
+  *reinterpret_cast<v4f *>(out + (size_t)t * rs.d + c) = acc;
 }
 
 }  // namespace fp8moe

@@ -98,7 +98,9 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
                          int32_t *ksplit);
 constexpr int kDownChannelsPerWave = 32;  // output channels per down-projection wave (nb 2)
-// out from y slabs summed in split order.
+constexpr int kMaxDownSplits = 8;         // K splits of the down projection (y slabs)
+// out from y slabs summed in split order (splits <= kMaxDownSplits, else
+// hipErrorInvalidValue).
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
                           const float *w, const int32_t *inv_pairs, float *out,
                           hipStream_t stream);

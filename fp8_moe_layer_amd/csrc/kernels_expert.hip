@@ -315,6 +315,7 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
 hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
                           const float *w, const int32_t *inv_pairs, float *out,
                           hipStream_t stream) {
+  if (splits < 1 || splits > kMaxDownSplits) return hipErrorInvalidValue;
   if (rs.T == 0) return hipSuccess;
   combine_kernel<<<dim3(rs.T, (rs.d + 1023) / 1024), 256, 0, stream>>>(rs, y, splits, ids, w,
                                                                       inv_pairs, out);
