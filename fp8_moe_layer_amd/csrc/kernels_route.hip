@@ -53,22 +53,59 @@ __global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict
   router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, wid - t * E, threadIdx.x & 63);
 }
 
-// Decode-sized batches: one workgroup per token computes its E logits (one
-// wave per expert at a time, the arithmetic of router_dot_wave, so the
-// logits equal those of moe_router_logits), quantises the token (expert 0's
-// wave) and, from the logits kept in LDS, picks its top-k with softmax
-// weights -- routing in one launch.
-__global__ __launch_bounds__(1024) void route_token_kernel(
+// Decode-sized batches: one workgroup per token computes its E logits (the
+// arithmetic of router_dot_wave, so the logits equal those of
+// moe_router_logits), quantises the token and, from the logits kept in LDS,
+// picks its top-k with softmax weights -- routing in one launch.  With
+// E * parts(d) <= 16 every (expert, part) has a wave of its own and the
+// token is quantised from the registers of expert 0's waves; otherwise each
+// wave walks its experts' parts.
+constexpr int kRouteWaves = 16;
+constexpr int kMaxDotParts = kRouteWaves;
+
+__global__ __launch_bounds__(kRouteWaves * kWave) void route_token_kernel(
     const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     int d, int E, int k_max, const int32_t *__restrict__ kpt, float *__restrict__ logits,
     uint8_t *__restrict__ xq, float *__restrict__ sx, int32_t *__restrict__ ids,
     float *__restrict__ w) {
   __shared__ float ls[kMaxExperts];
+  __shared__ float psum[kRouteWaves], pmax[kMaxDotParts];
   const int t = blockIdx.x, lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int e = wave; e < E; e += nw) {
-    const float lg = router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, e, lane);
-    if (lane == 0) ls[e] = lg;
+  const int parts = (d + kDotPart - 1) / kDotPart;
+  if (E * parts <= nw) {
+    const int e = wave / parts, part = wave - e * parts;  // wave-uniform
+    v4f xv[kDotVec];
+    if (e < E) {
+      float amax = 0.0f;
+      const float ps = router_part_wave(x + (size_t)t * d, wr + (size_t)e * d, d,
+                                        part * kDotPart, lane, xv, amax);
+      if (lane == 0) psum[wave] = ps;
+      if (e == 0) {
+        amax = wave_max(amax);
+        if (lane == 0) pmax[part] = amax;
+      }
+    }
+    __syncthreads();
+    if (e == 0 && xq) {  // expert 0's waves quantise their parts of the token from registers
+      float m = pmax[0];
+      for (int p = 1; p < parts; ++p) m = fmaxf(m, pmax[p]);
+      quantize_part_wave(xv, d, part * kDotPart, m, xq + (size_t)t * d, lane);
+      if (wave == 0 && lane == 0) sx[t] = m != 0.0f ? m / kE4m3Max : 1.0f;
+    }
+    // part sums in part order, as router_dot_wave adds them
+    for (int ee = threadIdx.x; ee < E; ee += blockDim.x) {
+      float lg = psum[ee * parts];
+      for (int p = 1; p < parts; ++p) lg = lg + psum[ee * parts + p];
+      if (bias) lg += bias[ee];
+      ls[ee] = lg;
+      logits[(size_t)t * E + ee] = lg;
+    }
+  } else {
+    for (int e = wave; e < E; e += nw) {
+      const float lg = router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, e, lane);
+      if (lane == 0) ls[e] = lg;
+    }
   }
   __syncthreads();
   if (wave == 0)
@@ -78,7 +115,7 @@ __global__ __launch_bounds__(1024) void route_token_kernel(
 
 // One workgroup per token pays off while a token's experts fit one wave each.
 bool route_fused_applies(int32_t T, int32_t E) {
-  return E <= 16 && (int64_t)T * E <= kRouterDotMax;
+  return E <= kRouteWaves && (int64_t)T * E <= kRouterDotMax;
 }
 
 hipError_t launch_route_topk_fused(const float *x, const float *w_router, const float *bias,
@@ -86,7 +123,9 @@ hipError_t launch_route_topk_fused(const float *x, const float *w_router, const 
                                    const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
                                    int32_t *ids, float *w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int nw = E < 16 ? E : 16;
+  // a wave per (expert, part) where they fit, else a wave per expert
+  const int parts = (d + kDotPart - 1) / kDotPart;
+  const int nw = E * parts <= kRouteWaves ? E * parts : (E < kRouteWaves ? E : kRouteWaves);
   route_token_kernel<<<T, nw * 64, 0, stream>>>(x, w_router, bias, d, E, k_max, kpt, logits, xq,
                                                 sx, ids, w);
   return hipGetLastError();

@@ -11,13 +11,53 @@
 namespace fp8moe {
 
 // ------------------------------------------------------------------ router, decode-sized
-// One wave computes the (token t, expert e) dot product over d, lanes
-// striding d by 4 floats with all of a lane's loads issued before the FMAs.
-// The wave of expert 0 also quantises its token's row (it has read it).
-constexpr int kDotVec = 8;  // float4 per lane per round: d <= 2048 in one round
+// d is cut into parts of kDotPart floats.  A wave sums a part with lanes
+// striding it 4 floats at a time (all of a lane's loads issued before its
+// FMAs), then a wave-wide sum; the logit is the sum of the part sums in part
+// order (+ bias).  So the logit is the same whether one wave walks the parts
+// or several waves take one part each.
+constexpr int kDotVec = 8;                 // float4 per lane per part
+constexpr int kDotPart = kDotVec * 4 * 64; // 2048 floats
 
-// Returns the logit (in every lane; the butterfly sum is bitwise the same
-// in all lanes).
+// One part starting at `base`: returns its sum (in every lane); x's values
+// stay in xv and their absolute maximum is folded into amax.
+__device__ __forceinline__ float router_part_wave(const float *__restrict__ xr,
+                                                  const float *__restrict__ w, int d, int base,
+                                                  int lane, v4f (&xv)[kDotVec], float &amax) {
+  v4f wv[kDotVec];
+#pragma unroll
+  for (int j = 0; j < kDotVec; ++j) {
+    const int i = base + (j * 64 + lane) * 4;
+    xv[j] = i < d ? *reinterpret_cast<const v4f *>(xr + i) : v4f{0.f, 0.f, 0.f, 0.f};
+    wv[j] = i < d ? *reinterpret_cast<const v4f *>(w + i) : v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kDotVec; ++j) {
+    acc = fmaf(xv[j].x, wv[j].x, acc);
+    acc = fmaf(xv[j].y, wv[j].y, acc);
+    acc = fmaf(xv[j].z, wv[j].z, acc);
+    acc = fmaf(xv[j].w, wv[j].w, acc);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv[j].x), fabsf(xv[j].y)),
+                             fmaxf(fabsf(xv[j].z), fabsf(xv[j].w))));
+  }
+  return wave_sum(acc);
+}
+
+// e4m3 codes of x's values in xv (one part), given the row's amax.
+__device__ __forceinline__ void quantize_part_wave(const v4f (&xv)[kDotVec], int d, int base,
+                                                   float amax, uint8_t *__restrict__ q, int lane) {
+  const float r = amax != 0.0f ? kE4m3Max / amax : 1.0f;
+#pragma unroll
+  for (int j = 0; j < kDotVec; ++j) {
+    const int i = base + (j * 64 + lane) * 4;
+    if (i < d) *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(xv[j].x * r, xv[j].y * r, xv[j].z * r, xv[j].w * r);
+  }
+}
+
+// The (token t, expert e) logit by one wave walking the parts; the wave of
+// expert 0 also quantises its token's row (re-reading it past one part).
+// Returns the logit in every lane.
 __device__ __forceinline__ float router_dot_wave(const float *__restrict__ x,
                                                  const float *__restrict__ wr,
                                                  const float *__restrict__ bias, int d, int E,
@@ -26,41 +66,27 @@ __device__ __forceinline__ float router_dot_wave(const float *__restrict__ x,
                                                  int t, int e, int lane) {
   const float *xr = x + (size_t)t * d;
   const float *w = wr + (size_t)e * d;
-  float acc = 0.0f, amax = 0.0f;
-  for (int base = 0; base < d; base += kDotVec * 256) {
-    v4f xv[kDotVec], wv[kDotVec];
-#pragma unroll
-    for (int j = 0; j < kDotVec; ++j) {
-      const int i = base + (j * 64 + lane) * 4;
-      xv[j] = i < d ? *reinterpret_cast<const v4f *>(xr + i) : v4f{0.f, 0.f, 0.f, 0.f};
-      wv[j] = i < d ? *reinterpret_cast<const v4f *>(w + i) : v4f{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int j = 0; j < kDotVec; ++j) {
-      acc = fmaf(xv[j].x, wv[j].x, acc);
-      acc = fmaf(xv[j].y, wv[j].y, acc);
-      acc = fmaf(xv[j].z, wv[j].z, acc);
-      acc = fmaf(xv[j].w, wv[j].w, acc);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(xv[j].x), fabsf(xv[j].y)),
-                               fmaxf(fabsf(xv[j].z), fabsf(xv[j].w))));
-    }
+  float logit = 0.0f, amax = 0.0f;
+  v4f xv[kDotVec];
+  for (int base = 0; base < d; base += kDotPart) {
+    const float ps = router_part_wave(xr, w, d, base, lane, xv, amax);
+    logit = base == 0 ? ps : logit + ps;
   }
-  acc = wave_sum(acc);
-  const float logit = bias ? acc + bias[e] : acc;
+  if (bias) logit += bias[e];
   if (lane == 0) logits[(size_t)t * E + e] = logit;
   if (e == 0 && xq) {
     amax = wave_max(amax);
-    float r = 1.0f, s = 1.0f;
-    if (amax != 0.0f) {
-      r = kE4m3Max / amax;
-      s = amax / kE4m3Max;
-    }
     uint8_t *q = xq + (size_t)t * d;
-    for (int i = lane * 4; i < d; i += kWave * 4) {
-      const v4f v = *reinterpret_cast<const v4f *>(xr + i);
-      *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x * r, v.y * r, v.z * r, v.w * r);
+    if (d <= kDotPart) {
+      quantize_part_wave(xv, d, 0, amax, q, lane);
+    } else {
+      const float r = amax != 0.0f ? kE4m3Max / amax : 1.0f;
+      for (int i = lane * 4; i < d; i += kWave * 4) {
+        const v4f v = *reinterpret_cast<const v4f *>(xr + i);
+        *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x * r, v.y * r, v.z * r, v.w * r);
+      }
     }
-    if (lane == 0) sx[t] = s;
+    if (lane == 0) sx[t] = amax != 0.0f ? amax / kE4m3Max : 1.0f;
   }
   return logit;
 }
