@@ -330,14 +330,27 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
         const int ks = ks0 + s;
         const int c = ks / C::KSC;
         const uint8_t *fa = lds_lane + (c % C::NBUF) * C::BYTES + (ks - c * C::KSC) * 2048;
+        // Row groups in batches of MB: a batch's activation fragments are
+        // all read from LDS before its MFMAs (groups past msub inside a
+        // batch hold the loader's zero pieces).  Two-operand waves only:
+        // four-operand ones have no registers to spare.
+        constexpr int MB = (NB == 2 && MSUB >= 4) ? 4 : 1;
 #pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
-          if (m < msub) {
-            const v4i a0 = *reinterpret_cast<const v4i *>(fa + m * C::KSC * 2048);
-            const v4i a1 = *reinterpret_cast<const v4i *>(fa + m * C::KSC * 2048 + 1024);
-            const v8i a = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        for (int mb = 0; mb < MSUB; mb += MB) {
+          if (mb < msub) {
+            v8i a[MB];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[m][nb] = mfma_e4m3_16x16x128(a, ring[s][nb], acc[m][nb]);
+            for (int j = 0; j < MB; ++j) {
+              const v4i a0 = *reinterpret_cast<const v4i *>(fa + (mb + j) * C::KSC * 2048);
+              const v4i a1 = *reinterpret_cast<const v4i *>(fa + (mb + j) * C::KSC * 2048 + 1024);
+              a[j] = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            }
+            if (MB > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[mb + j][nb] = mfma_e4m3_16x16x128(a[j], ring[s][nb], acc[mb + j][nb]);
           }
         }
         load_b(ring[s], ks + C::PF);
