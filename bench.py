@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--no-requant", action="store_true")
     p.add_argument("--zipf-sweep", action="store_true",
                    help="qwen3: also time T=64 at several Zipf router biases (distinct experts 16..128)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the layer captured in a HIP graph (one graph per weight copy)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -103,6 +105,40 @@ class HipEvents:
     def close(self):
         for h in self.ev:
             self.hip.hipEventDestroy(h)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_peaks(torch, dev) -> dict:
+    """The device as measured next to the spec-sheet peaks: compute units, and
+    the bytes read + written per second by a plain 1 GiB device copy (a
+    STREAM-like probe; the spec peak stays the roofline's denominator)."""
+    props = torch.cuda.get_device_properties(dev)
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    s = start.elapsed_time(end) * 1e-3 / reps
+    del src, dst
+    return {"compute_units": props.multi_processor_count, "arch": getattr(props, "gcnArchName", ""),
+            "copy_GBps": round(2 * n * 4 / s / 1e9, 1),
+            "copy_note": "1 GiB device copy, read + write bytes over time (torch copy kernel)"}
 
 
 def kernel_source_hash() -> str:
@@ -295,7 +331,38 @@ def main():
     roofline.update({"traffic": stored_traffic(workload), "kernel": "wsgemm_kernel (gate/up)",
                      "alg_bytes_per_launch": gu_bytes, "fp8_flops_per_launch": gu_flops,
                      "avg_launch_us": stages_us["gate_up"], "timing": "hipEvents around the launch, "
-                     "recorded by the library on its stream"})
+                     "recorded by the library on its stream",
+                     "measured": measured_peaks(torch, dev)})
+
+    # ---- the same steps replayed from HIP graphs (launch overhead removed)
+    graph = None
+    if args.graph:
+        gs = []
+        cap = torch.cuda.Stream()  # default priority
+        for lay in layers:
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                lay.forward(x, k_per_token=kpt, out=out, topk_ids=ids)
+            torch.cuda.current_stream().wait_stream(cap)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                lay.forward(x, k_per_token=kpt, out=out, topk_ids=ids)
+            gs.append(g)
+        for i in range(args.warmup):
+            gs[i % len(gs)].replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(args.steps):
+            gs[i % len(gs)].replay()
+        end.record()
+        torch.cuda.synchronize()
+        gms = start.elapsed_time(end) / args.steps
+        graph = {"us_per_step": round(gms * 1e3, 2), "eager_us_per_step": round(ms * 1e3, 2),
+                 "tokens_per_s": round(T / (gms * 1e-3), 1), "graphs": len(gs)}
+        log(f"graph replay: {graph}")
+        del gs
 
     # ---- batch sweep (same weights)
     sweep = None
@@ -362,10 +429,10 @@ def main():
         ks_all = None if kpt is None else kpt.cpu().numpy()
         bias_np = None if ri.router_bias is None else ri.router_bias.numpy()
 
-        def run_oracle(n):
+        def run_oracle(n, nthreads=cores):
             ks = None if ks_all is None else ks_all[:n]
             return oracle.forward(xs_all[:n], qw, spec.k, w_router=ri.w_router.numpy(),
-                                  router_bias=bias_np, k_per_token=ks, nthreads=cores)
+                                  router_bias=bias_np, k_per_token=ks, nthreads=nthreads)
 
         # size the sample for ~cpu_seconds of oracle work: probe, then scale
         n = min(T, max(1, 4 * cores // max(1, spec.k)))
@@ -386,10 +453,17 @@ def main():
         for _ in range(reps):
             ref, ido, _ = run_oracle(n)
         wall = time.time() - t0
+        # the same oracle on one thread, over a 1/cores share of the sample
+        n1 = max(1, n // cores)
+        t0 = time.time()
+        run_oracle(n1, 1)
+        wall1 = time.time() - t0
         cpu = {"value": round(n * reps / wall, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                "sample": f"first {n} of the {T} tokens, full layer incl. router, repeated {reps}x "
                          f"(the oracle quantises its own weights beforehand, untimed)",
-               "seconds": round(wall, 2)}
+               "seconds": round(wall, 2), "cpu_model": cpu_model(),
+               "single_thread": {"value": round(n1 / wall1, 3), "unit": "tokens/s",
+                                 "sample": f"first {n1} tokens", "seconds": round(wall1, 2)}}
         got = out[:n].cpu().numpy().astype(np.float64)
         parity = {"rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
                   "ids_equal": bool(np.array_equal(ids_np[:n], ido)), "tokens": n}
@@ -419,6 +493,7 @@ def main():
                   "fp8_flops": flops, "mfma_frac": round(flops / (ms * 1e-3) / PEAK_FP8, 5)},
         "step_us": step_us,
         "stages_us": stages_us,
+        **({"graph": graph} if graph else {}),
         "parity": parity,
     }
     if sweep:

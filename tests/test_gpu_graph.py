@@ -1,0 +1,55 @@
+"""The fused layer captured in a HIP graph (torch.cuda.CUDAGraph over the
+library's launches on the capture stream): every replay must equal the eager
+forward on the same input, bit for bit, with eager work, input changes and
+synchronisations between the replays.  The layer's launches are kernels
+only (no memset, allocation or synchronisation), which is what makes them
+capturable; the workspace and the output are allocated before capture."""
+import pytest
+import torch
+
+import workloads as wl
+from gpu_common import Layer, dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SPECS = {
+    "tiny": wl.TINY,
+    "zipf-two-shapes": wl.TINY.with_(T=64, d=512, f=256, E=128, k=8, bias="zipf", bias_param=2.0),
+    "shared-elastic": wl.TINY.with_(T=48, d=256, f=192, E=16, k=4, n_shared=2, k_choices=(1, 2, 4)),
+}
+
+
+def _capture(layer, x, kpt, out):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, k_per_token=kpt, out=out)  # workspace allocated before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, k_per_token=kpt, out=out)
+    return g
+
+
+@pytest.mark.parametrize("name", list(SPECS))
+@pytest.mark.parametrize("msub", [None, 16])
+def test_graph_replays_match_eager(name, msub, monkeypatch):
+    if msub is not None:
+        monkeypatch.setenv("FP8MOE_MSUB", str(msub))  # 256-row passes as at prefill
+    L = Layer(SPECS[name], want_oracle=False)
+    layer = L.layer()
+    x = L.x.clone()
+    out = torch.empty((x.shape[0], L.spec.d), dtype=torch.float32, device=dev())
+    g = _capture(layer, x, L.kpt, out)
+    gen = torch.Generator(device=dev()).manual_seed(7)
+    for rep in range(4):
+        if rep % 2 == 1:  # a new input in the captured buffer
+            x.copy_(torch.randn(x.shape, generator=gen, device=dev()))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = layer.forward(x.clone(), k_per_token=L.kpt)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager forward"
+    del g
