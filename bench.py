@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--no-requant", action="store_true")
     p.add_argument("--zipf-sweep", action="store_true",
                    help="qwen3: also time T=64 at several Zipf router biases (distinct experts 16..128)")
+    p.add_argument("--group", action="store_true",
+                   help="qwen3: decode batches of 64 from a pool of 512 tokens, in arrival order "
+                        "and grouped by expert affinity (moe_group_tokens)")
     p.add_argument("--graph", action="store_true",
                    help="also time the layer captured in a HIP graph (one graph per weight copy)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -380,6 +383,47 @@ def main():
 
     # ---- Qwen3-shaped decode at several router biases (distinct active experts)
     zipf = None
+    # ---- decode batches from a token pool: arrival order vs grouped by expert affinity
+    grouping = None
+    if args.group and cfg == "qwen3":
+        grouping = []
+        pool, gb = 512, 64
+        for alpha in (0.0, 1.0, 1.5):
+            gs_ = wl.SPECS[cfg].with_(T=pool, bias_param=alpha)
+            gri = wl.routing_inputs(gs_, args.seed)
+            gbias = None if gri.router_bias is None else gri.router_bias.to(dev)
+            glay = fp8.MoELayer(dw, gri.w_router.to(dev), gs_.k, gbias)
+            gx = gri.x.to(dev)
+            gid = torch.empty((pool, gs_.k), dtype=torch.int32, device=dev)
+            glay.forward(gx, topk_ids=gid)
+            gi = gid.cpu().numpy()
+            t0 = time.time()
+            order = fp8.group_tokens(gi, E, gb)
+            host_ms = (time.time() - t0) * 1e3
+            entry = {"alpha": alpha, "pool": pool, "batch": gb, "group_host_ms": round(host_ms, 2)}
+            for mode, idx in (("arrival", np.arange(pool)), ("grouped", order)):
+                bx = [gx[torch.as_tensor(idx[b:b + gb], device=dev, dtype=torch.long)].contiguous()
+                      for b in range(0, pool, gb)]
+                Ds = [int(len(np.unique(gi[idx[b:b + gb]][gi[idx[b:b + gb]] >= 0]))) for b in range(0, pool, gb)]
+                bout = torch.empty((gb, d), dtype=torch.float32, device=dev)
+                for i in range(args.warmup):
+                    glay.forward(bx[i % len(bx)], out=bout)
+                ev = HipEvents(2)
+                torch.cuda.synchronize()
+                rounds = max(1, args.steps // len(bx))
+                ev.record(0, sh)
+                for r in range(rounds):
+                    for xb in bx:
+                        glay.forward(xb, out=bout)
+                ev.record(1, sh)
+                torch.cuda.synchronize()
+                bms = ev.elapsed_ms(0, 1) / (rounds * len(bx))
+                ev.close()
+                entry[mode] = {"mean_distinct_experts": round(float(np.mean(Ds)), 1),
+                               "us_per_batch": round(bms * 1e3, 1)}
+            grouping.append(entry)
+            log(f"grouping alpha={alpha}: {entry}")
+
     if args.zipf_sweep and cfg == "qwen3":
         zipf = []
         zcopies = []
@@ -500,6 +544,8 @@ def main():
         res["sweep"] = sweep
     if zipf:
         res["zipf_sweep"] = zipf
+    if grouping is not None:
+        res["grouping"] = grouping
     print(json.dumps(res), flush=True)
 
 

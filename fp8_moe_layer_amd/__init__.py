@@ -70,6 +70,7 @@ _status_str = _sig("moe_status_str", C.c_char_p, _i32)
 _last_error = _sig("moe_last_error", C.c_char_p)
 _abi_version = _sig("moe_abi_version", _i32)
 _debug_stage_events = _sig("moe_debug_stage_events", _i32, C.POINTER(_vp), _i32)
+_group_tokens = _sig("moe_group_tokens", _i32, _vp, _i32, _i32, _i32, _i32, _vp)
 
 N_STAGE_EVENTS = 8
 STAGES = ("route", "topk", "permute", "gate_up", "requant", "down", "combine")
@@ -170,6 +171,22 @@ def route_topk(logits, k_max: int, k_per_token=None, stream=None):
     _check(_route_topk(_ptr(logits, torch.float32), T, E, k_max, _ptr(k_per_token, torch.int32),
                        _ptr(ids), _ptr(w), _stream(stream)))
     return ids, w
+
+
+def group_tokens(topk_ids, E: int, batch: int):
+    """Order a token pool into decode batches of `batch` tokens that activate
+    few distinct experts (moe_group_tokens; host computation).  topk_ids:
+    [n, k] int32 routing (numpy or a torch tensor, copied to the host).
+    Returns the order, an int32 numpy permutation of range(n)."""
+    import numpy as np
+    if isinstance(topk_ids, torch.Tensor):
+        topk_ids = topk_ids.detach().cpu().numpy()
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    n, k = ids.shape
+    order = np.empty(n, dtype=np.int32)
+    _check(_group_tokens(ids.ctypes.data if n else None, n, k, E, batch,
+                         order.ctypes.data if n else None))
+    return order
 
 
 def capacity(T: int, E: int, k_max: int, block_m: int) -> int:

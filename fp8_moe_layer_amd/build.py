@@ -14,7 +14,7 @@ HERE = pathlib.Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
 LIB = HERE / "libfp8moe.so"
 SOURCES = ["kernels_route.hip", "kernels_permute.hip", "kernels_expert.hip", "kernels_persistent.hip",
-           "abi.hip"]
+           "abi.hip", "batching.hip"]
 ARCH = os.environ.get("FP8MOE_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

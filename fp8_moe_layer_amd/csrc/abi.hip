@@ -33,6 +33,23 @@ moe_status ok() {
   return MOE_OK;
 }
 
+}  // namespace
+
+// The error text of the calling thread, for host-side entry points defined
+// in other files.
+namespace fp8moe {
+moe_status fail_status(moe_status code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+moe_status ok_status() { return ok(); }
+}  // namespace fp8moe
+
+namespace {
+
 moe_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return MOE_OK;
   return fail(MOE_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -5,7 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/fp8moe.h"
+
 namespace fp8moe {
+
+// Set the calling thread's error text (moe_last_error) and return `code`;
+// ok_status clears it and returns MOE_OK.
+moe_status fail_status(moe_status code, const char *fmt, ...);
+moe_status ok_status();
 
 // One unit of grouped-GEMM work: `rows` consecutive expert rows starting at
 // `row0` of the expert-rows layout, all belonging to `expert` (e >= E means

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FP8MOE_ABI_VERSION 2
+#define FP8MOE_ABI_VERSION 3
 
 typedef int32_t moe_status;
 enum {
@@ -233,6 +233,24 @@ moe_status moe_fused_forward(const moe_dims *dims /*host*/, const float *x, cons
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Decode batching by expert affinity ("ELDR : Microsoft et KAIST accélèrent
+ * le décodage des MoE": a decode step loads the weights of every distinct
+ * expert its batch activates; changing only which tokens share a batch
+ * changes no token's output).  Orders a pool of n tokens, given their
+ * routing, into batches of `batch` tokens (the last one shorter when n is
+ * not a multiple) that activate few distinct experts: each batch starts
+ * from the lowest-numbered unplaced token, then repeatedly takes the
+ * unplaced token that adds the fewest experts not yet in the batch (ties:
+ * the lowest number).  Deterministic.  HOST memory: ids [n][k] (-1 = empty
+ * slot, else in [0, E); a repeated id counts once), order [n] out, a
+ * permutation of 0..n-1 -- batch b is order[b*batch .. min(n, (b+1)*batch)).
+ * Synchronous, no device work, no allocation visible to the caller.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (also for an id outside [-1, E)). */
+moe_status moe_group_tokens(const int32_t *ids /*host*/, int32_t n, int32_t k, int32_t E,
+                            int32_t batch, int32_t *order /*host*/);
+
 /* ------------------------------------------------------------------------ */
 
 /* Stage timing (instrumentation, not part of the layer).  After this call,

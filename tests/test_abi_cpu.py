@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.ABI_VERSION == 2
+    assert fp8.ABI_VERSION == 3
     assert fp8._status_str(0) == b"ok"
     assert fp8._status_str(ERR_WORKSPACE) == b"workspace too small"
     assert fp8._status_str(99) == b"unknown status"
