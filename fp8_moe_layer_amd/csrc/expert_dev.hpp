@@ -9,18 +9,22 @@
 //
 // Grouped GEMM schedule: weight-stationary, one workgroup per (work item,
 // tile of output channels[, K split]).  A work item is an expert and up to
-// 16*MSUB of its rows, so a decode-sized batch puts all of an expert's rows
-// in one item and each active expert's weights cross HBM exactly once.
+// 16*MSUB of its rows (16*ML with the two-shape kernel), so a decode-sized
+// batch puts all of an expert's rows in one item and each active expert's
+// weights cross HBM exactly once.
 //
-// Workgroup = 4 compute waves + 1 loader wave (320 lanes):
-//  - the loader wave gathers the item's activation rows (e4m3) into a ring of
-//    four 16 KB LDS chunks with global_load_lds_dwordx4, three chunks ahead
-//    of the compute waves (exact vmcnt waits, so only the chunk due next is
-//    waited for);
-//  - each compute wave streams its own weight rows (16 output channels; the
-//    gate and the up row of each for the gate/up GEMM) straight from HBM
-//    into registers through a PF-deep prefetch ring, reads the activation
-//    fragments from LDS and runs v_mfma_f32_16x16x128_f8f6f4;
+// Workgroup = W compute waves (1..8, chosen by the host) + 1 loader wave
+// (2 for 256-row passes):
+//  - the loader gathers the item's activation rows (e4m3) into a ring of four
+//    LDS chunks with global_load_lds_dwordx4, three chunks ahead of the
+//    compute waves (exact vmcnt waits, so only the chunk due next is waited
+//    for), after one batch of row lookups; the rows' activation scales go to
+//    an LDS table by direct-to-LDS dword loads issued ahead of the first
+//    chunk;
+//  - each compute wave streams NB weight operands of 16 rows (gate and up
+//    rows of 16 channels, or 32 down channels) from HBM into registers
+//    through a PF-deep prefetch ring, reads the activation fragments from LDS
+//    (four row groups at a time) and runs v_mfma_f32_16x16x128_f8f6f4;
 //  - one s_barrier per chunk hands buffers between them.  The compute side
 //    waits only on LDS counters, so its weight prefetches stay in flight
 //    across it.
