@@ -278,22 +278,31 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   }
 
   // ---------------- compute waves
+  // Operand nb: weight rows of output channel ch[nb] (gate, up, gate, ...
+  // for gate/up; down channels otherwise) and that channel's weight scale,
+  // loaded here so the epilogue waits on no global load.  A lane past the
+  // last channel (partial last tile) reads valid rows and stores nothing.
   const uint8_t *bw[NB];
   int ch[NB];
+  float wsc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     int o;
     const uint8_t *wbase;
+    const float *sbase;
     if (GATEUP) {
       o = tile * CH_WG + wave * CH_WAVE + (nb >> 1) * 16 + ln;
       wbase = ((nb & 1) == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
               ex * (size_t)N * KT * 128;
+      sbase = (nb & 1) == 0 ? (shared ? g.w.ss_gate : g.w.s_gate) : (shared ? g.w.ss_up : g.w.s_up);
     } else {
       o = tile * CH_WG + wave * CH_WAVE + nb * 16 + ln;
       wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * KT * 128;
+      sbase = shared ? g.w.ss_down : g.w.s_down;
     }
+    const int orow = o < N ? o : N - 1;
     ch[nb] = o;
-    const int orow = o < N ? o : N - 1;  // a partial last tile re-reads a valid row
+    wsc[nb] = sbase[ex * N + orow];
     // tile order: 16 rows x 128 K bytes per 2 KB tile, lane l at l*16 and 1024 + l*16
     bw[nb] = wbase + ((size_t)(orow >> 4) * KT + (k_begin >> 7)) * 2048 + lane * 16;
   }
@@ -363,55 +372,49 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
     }
 
     // ---------------- epilogue
+    // Lane (ln, kg) holds rows m*16 + kg*4 + i of channel ch[nb].  Only the
+    // last row group of a pass can run past the item's rows; a padding row
+    // has scale 0 (and zero activations): 0 out.
+    // Stores are non-temporal: the output stream does not push the weight
+    // stream's neighbours (activation rows, tables) out of L2.
     if (GATEUP) {
 #pragma unroll
       for (int cg = 0; cg < NB / 2; ++cg) {
-        const int o = ch[2 * cg];
-        const bool live = o < N;  // a partial last tile computes a clamped row
-        const float sgo = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + (live ? o : N - 1)];
-        const float suo = (shared ? g.w.ss_up : g.w.s_up)[ex * N + (live ? o : N - 1)];
+        if (ch[2 * cg] >= N) continue;
+        const float sgo = wsc[2 * cg], suo = wsc[2 * cg + 1];
+        float *hp = g.out + (size_t)(row0 + p0 + kg * 4) * N + ch[2 * cg];
 #pragma unroll
         for (int m = 0; m < MSUB; ++m) {
           if (m < msub) {
+            const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+            const int rlim = prow - (m * 16 + kg * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int r = p0 + m * 16 + kg * 4 + i;
-              if (r < rows && live) {
-                // a padding row has scale 0 (and zero activations): h = 0
-                const float sxt = rsc[m * 16 + kg * 4 + i];
-                const float gv = acc[m][2 * cg][i] * sxt * sgo;
-                const float uv = acc[m][2 * cg + 1][i] * sxt * suo;
-                // non-temporal: the store stream does not push the weight
-                // stream's neighbours (activation rows, tables) out of L2
-                __builtin_nontemporal_store(gv / (1.0f + expf(-gv)) * uv,
-                                            &g.out[(size_t)(row0 + r) * N + o]);
-              }
+              const float gv = acc[m][2 * cg][i] * sx4[i] * sgo;
+              const float uv = acc[m][2 * cg + 1][i] * sx4[i] * suo;
+              // SiLU(g)*u with the reciprocal instruction (1 ulp) for the
+              // divide
+              const float hv = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
+              if (m < msub - 1 || i < rlim) __builtin_nontemporal_store(hv, hp + (size_t)(m * 16 + i) * N);
             }
           }
         }
       }
     } else {
-      const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * N;
-      float sdv[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sdv[nb] = sd[ch[nb] < N ? ch[nb] : N - 1];
-      float *ys = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N;
+      float *yp = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
 #pragma unroll
       for (int m = 0; m < MSUB; ++m) {
         if (m < msub) {
+          const v4f sh4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+          const int rlim = prow - (m * 16 + kg * 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = p0 + m * 16 + kg * 4 + i;
-            if (r < rows) {
-              // a padding row has scale 0 (and zero activations): y = 0
-              const float shr = rsc[m * 16 + kg * 4 + i];
-              const int grow = row0 + r;
+            if (m < msub - 1 || i < rlim) {
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) {
-                if (ch[nb] < N)  // non-temporal, as h above
-                  __builtin_nontemporal_store(acc[m][nb][i] * shr * sdv[nb],
-                                              &ys[(size_t)grow * N + ch[nb]]);
-              }
+              for (int nb = 0; nb < NB; ++nb)
+                if (ch[nb] < N)
+                  __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wsc[nb],
+                                              yp + (size_t)(m * 16 + i) * N + ch[nb]);
             }
           }
         }
