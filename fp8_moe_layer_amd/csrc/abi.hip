@@ -209,9 +209,13 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
   const int nb_first = (forced_nb == 4 && msub <= 8) ? 4 : 2;
   for (int nb = nb_first; nb >= 2; nb -= 2) {
     const int ch_wave = gate_up ? 8 * nb : 16 * nb;
-    const int maxw = msub > 8 ? kGemmMaxWaves16 : nb > 2 ? kGemmMaxThreadsWide / 64 - 1 : kGemmMaxWaves;
+    // 256-row passes: the prefill kernel's eight waves, or a forced wave
+    // count on the loader-wave kernel (at most six computing waves)
+    const int maxw = msub > 8 ? (forced >= 1 ? kGemmMaxWaves16 : kPfWaves)
+                              : nb > 2 ? kGemmMaxThreadsWide / 64 - 1 : kGemmMaxWaves;
     for (int W = maxw; W >= 1; --W) {
       if (forced >= 1 && forced <= maxw && W != forced) continue;
+      if (msub > 8 && forced < 1 && W != kPfWaves) continue;
       const int per_cu = (nb == 2 && W <= 5 && msub <= 8) ? 2 : 1;
       const double slots = (double)kCUs * per_cu;
       const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);

@@ -113,6 +113,127 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 // past the end.  Never written (each translation unit has its own copy).
 static __device__ __attribute__((aligned(64))) uint8_t g_zero_piece[64];
 
+// Weight operands of one compute wave.  Operand nb holds the weight rows of
+// output channel ch[nb] (gate, up, gate, ... for gate/up; down channels
+// otherwise), read as MFMA B operands; wsc[nb] is that channel's weight
+// scale, loaded at set-up so the epilogue waits on no global load.  A lane
+// past the last channel (partial last tile) reads valid rows and stores
+// nothing.
+template <int NB, bool GATEUP, bool NT>
+struct WOperands {
+  const uint8_t *bw[NB];
+  int ch[NB];
+  float wsc[NB];
+  int nks;  // K steps of this split
+
+  // c0: the wave's first output channel; k_begin: first K byte of the split.
+  __device__ __forceinline__ void init(const GemmArgs &g, bool shared, size_t ex, int c0, int k_begin,
+                                       int nks_, int lane) {
+    const int N = GATEUP ? g.rs.f : g.rs.d;
+    const int K = GATEUP ? g.rs.d : g.rs.f;
+    const int KT = (K + 127) >> 7;  // weight tiles along K
+    nks = nks_;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int o;
+      const uint8_t *wbase;
+      const float *sbase;
+      if (GATEUP) {
+        o = c0 + (nb >> 1) * 16 + (lane & 15);
+        wbase = ((nb & 1) == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
+                ex * (size_t)N * KT * 128;
+        sbase = (nb & 1) == 0 ? (shared ? g.w.ss_gate : g.w.s_gate) : (shared ? g.w.ss_up : g.w.s_up);
+      } else {
+        o = c0 + nb * 16 + (lane & 15);
+        wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * KT * 128;
+        sbase = shared ? g.w.ss_down : g.w.s_down;
+      }
+      const int orow = o < N ? o : N - 1;
+      ch[nb] = o;
+      wsc[nb] = sbase[ex * N + orow];
+      // tile order: 16 rows x 128 K bytes per 2 KB tile, lane l at l*16 and 1024 + l*16
+      bw[nb] = wbase + ((size_t)(orow >> 4) * KT + (k_begin >> 7)) * 2048 + lane * 16;
+    }
+  }
+
+  // Weight tile of K step ks: two contiguous 1 KB halves.  Past the end the
+  // step is clamped to the last one (its activation pieces are zero); the
+  // zero padding of a 64-byte tail step meets zero activation pieces.
+  __device__ __forceinline__ void load(v8i (&b)[NB], int ks) const {
+    ks = min(ks, nks - 1);
+    const int o0 = ks * 2048;
+    const int o1 = o0 + 1024;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const v4i lo = NT ? load16_nt(bw[nb] + o0) : load16(bw[nb] + o0);
+      const v4i hi = NT ? load16_nt(bw[nb] + o1) : load16(bw[nb] + o1);
+      b[nb] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  }
+};
+
+// Epilogue of one row pass (rows p0 .. p0+prow-1 of the item starting at
+// expert row row0): gate/up writes h = SiLU(g)*u, the down projection its
+// split's y slab.  rsc: the pass's activation scale per row (0 for a
+// padding row) in LDS.
+template <int MSUB, int NB, bool GATEUP, bool NT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc)[MSUB][NB],
+                                              const WOperands<NB, GATEUP, NT> &wo, const float *rsc,
+                                              int row0, int p0, int prow, int msub, int split,
+                                              int lane) {
+  const RowSpace &rs = g.rs;
+  const int N = GATEUP ? rs.f : rs.d;
+  const int kg = lane >> 4;
+  // Lane (ln, kg) holds rows m*16 + kg*4 + i of channel wo.ch[nb].  Only the
+  // last row group of a pass can run past the item's rows; a padding row
+  // has scale 0 (and zero activations): 0 out.
+  // Stores are non-temporal: the output stream does not push the weight
+  // stream's neighbours (activation rows, tables) out of L2.
+  if (GATEUP) {
+#pragma unroll
+    for (int cg = 0; cg < NB / 2; ++cg) {
+      if (wo.ch[2 * cg] >= N) continue;
+      const float sgo = wo.wsc[2 * cg], suo = wo.wsc[2 * cg + 1];
+      float *hp = g.out + (size_t)(row0 + p0 + kg * 4) * N + wo.ch[2 * cg];
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) {
+        if (m < msub) {
+          const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+          const int rlim = prow - (m * 16 + kg * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[m][2 * cg][i] * sx4[i] * sgo;
+            const float uv = acc[m][2 * cg + 1][i] * sx4[i] * suo;
+            // SiLU(g)*u with the reciprocal instruction (1 ulp) for the
+            // divide
+            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
+            if (m < msub - 1 || i < rlim) __builtin_nontemporal_store(hv, hp + (size_t)(m * 16 + i) * N);
+          }
+        }
+      }
+    }
+  } else {
+    float *yp = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m) {
+      if (m < msub) {
+        const v4f sh4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+        const int rlim = prow - (m * 16 + kg * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (m < msub - 1 || i < rlim) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              if (wo.ch[nb] < N)
+                __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wo.wsc[nb],
+                                            yp + (size_t)(m * 16 + i) * N + wo.ch[nb]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 
 template <int MSUB>
@@ -189,7 +310,6 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   // activation pieces by a repeat of the last weight step.
   const int nks_pf = (nks + C::PF - 1) / C::PF * C::PF;
   const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;  // LDS chunks of KSC steps
-  const int KT = (K + 127) >> 7;                        // weight tiles along K
 
   const bool shared = expert >= rs.E;
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
@@ -278,48 +398,8 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   }
 
   // ---------------- compute waves
-  // Operand nb: weight rows of output channel ch[nb] (gate, up, gate, ...
-  // for gate/up; down channels otherwise) and that channel's weight scale,
-  // loaded here so the epilogue waits on no global load.  A lane past the
-  // last channel (partial last tile) reads valid rows and stores nothing.
-  const uint8_t *bw[NB];
-  int ch[NB];
-  float wsc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    int o;
-    const uint8_t *wbase;
-    const float *sbase;
-    if (GATEUP) {
-      o = tile * CH_WG + wave * CH_WAVE + (nb >> 1) * 16 + ln;
-      wbase = ((nb & 1) == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
-              ex * (size_t)N * KT * 128;
-      sbase = (nb & 1) == 0 ? (shared ? g.w.ss_gate : g.w.s_gate) : (shared ? g.w.ss_up : g.w.s_up);
-    } else {
-      o = tile * CH_WG + wave * CH_WAVE + nb * 16 + ln;
-      wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * KT * 128;
-      sbase = shared ? g.w.ss_down : g.w.s_down;
-    }
-    const int orow = o < N ? o : N - 1;
-    ch[nb] = o;
-    wsc[nb] = sbase[ex * N + orow];
-    // tile order: 16 rows x 128 K bytes per 2 KB tile, lane l at l*16 and 1024 + l*16
-    bw[nb] = wbase + ((size_t)(orow >> 4) * KT + (k_begin >> 7)) * 2048 + lane * 16;
-  }
-  // Weight tile of k step ks: two contiguous 1 KB halves.  Past the end the
-  // step is clamped to the last one (its activation pieces are zero); the
-  // zero padding of a 64-byte tail step meets zero activation pieces.
-  auto load_b = [&](v8i (&b)[NB], int ks) {
-    ks = min(ks, nks - 1);
-    const int o0 = ks * 2048;
-    const int o1 = o0 + 1024;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const v4i lo = NT ? load16_nt(bw[nb] + o0) : load16(bw[nb] + o0);
-      const v4i hi = NT ? load16_nt(bw[nb] + o1) : load16(bw[nb] + o1);
-      b[nb] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-  };
+  WOperands<NB, GATEUP, NT> wo;
+  wo.init(g, shared, ex, tile * CH_WG + wave * CH_WAVE, k_begin, nks, lane);
 
   v8i ring[C::PF][NB];
   v4f acc[MSUB][NB];
@@ -334,7 +414,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[m][nb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < C::PF; ++s) load_b(ring[s], s);
+    for (int s = 0; s < C::PF; ++s) wo.load(ring[s], s);
     barrier_lds();
 
     for (int ks0 = 0; ks0 < nks_pf; ks0 += C::PF) {
@@ -366,60 +446,202 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
                 acc[mb + j][nb] = mfma_e4m3_16x16x128(a[j], ring[s][nb], acc[mb + j][nb]);
           }
         }
-        load_b(ring[s], ks + C::PF);
+        wo.load(ring[s], ks + C::PF);
         if ((ks + 1) % C::KSC == 0 || ks + 1 == nks_pf) barrier_lds();  // end of chunk c
       }
     }
 
-    // ---------------- epilogue
-    // Lane (ln, kg) holds rows m*16 + kg*4 + i of channel ch[nb].  Only the
-    // last row group of a pass can run past the item's rows; a padding row
-    // has scale 0 (and zero activations): 0 out.
-    // Stores are non-temporal: the output stream does not push the weight
-    // stream's neighbours (activation rows, tables) out of L2.
-    if (GATEUP) {
+    gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
+  }
+}
+
+
+// ------------------------------------------------------------------ prefill grouped GEMM
+// Row passes of 256 rows (prefill-sized batches re-read an expert's weights
+// once per pass, so passes are as tall as LDS allows).  Eight waves, two per
+// SIMD, and every wave both gathers and computes: wave w gathers row groups
+// 2w and 2w+1 of each chunk (four direct-to-LDS loads) and computes 16
+// gate/up channels (32 down channels) over all 256 rows.  A split into
+// loader and compute waves left two SIMDs with one computing wave each.
+//
+// Per K step every wave issues its loads in one fixed order, gather of chunk
+// ks+3 then weights of step ks+2, with scheduling fences between them, so
+// the number of loads issued after a given chunk's gather is a constant:
+// vmcnt(16) before the end-of-step barrier means this wave's part of chunk
+// ks+1 has landed, and after the barrier every wave's part has.  Gathers
+// past the last chunk read the zero piece into the buffer just freed, which
+// keeps that count constant to the end of the pass.
+//
+// The gathers are issued in inline assembly (dma_lds16/dma_lds4 below): the
+// compiler's wait-count pass, when it sees direct-to-LDS loads in a wave
+// that also reads LDS, waits for every outstanding load before the LDS
+// reads, which empties the gather pipeline every step.  Invisible to it,
+// they only make its waits for the weight registers stricter than needed
+// (those waits then also cover the gather issued two steps earlier).  The
+// four ring buffers are separate LDS arrays, the K loop unrolled by four.
+struct PfChunk {
+  static constexpr int MSUB = 16;
+  static constexpr int MP = 16 * MSUB;  // rows per pass
+  static constexpr int BYTES = MP * 128;  // one K step of the pass's rows: 32 KB
+  static constexpr int NBUF = 4;          // LDS ring; gathers run three chunks ahead
+  static constexpr int PF = 2;            // weight prefetch depth in K steps
+  static constexpr int TABLE = 2 * MP;    // scale table floats, one copy per pass parity
+};
+
+// Direct-to-LDS loads in inline assembly: 16 bytes per lane to lds + 16*lane
+// (dma_lds16) or 4 bytes to lds + 4*lane (dma_lds4); lds is a wave-uniform
+// LDS address.  The caller waits for them with s_waitcnt vmcnt.  They set
+// M0 themselves, so code using them must issue no other direct-to-LDS load
+// (the compiler keeps no value in M0 across them otherwise: M0 is written
+// right before each of its own uses).
+__device__ __forceinline__ void dma_lds16(const void *src, void *lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(a)
+               : "memory");
+}
+__device__ __forceinline__ void dma_lds4(const void *src, void *lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(a)
+               : "memory");
+}
+
+template <bool GATEUP>
+__device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *b0, uint8_t *b1,
+                                        uint8_t *b2, uint8_t *b3, float *row_scale) {
+  using C = PfChunk;
+  constexpr int MSUB = C::MSUB, NB = 2, NW = kPfWaves;
+  constexpr int CH_WAVE = GATEUP ? 16 : 32;
+  constexpr int CH_WG = NW * CH_WAVE;
+  const RowSpace &rs = g.rs;
+  const int K = GATEUP ? rs.d : rs.f;
+  const int N = GATEUP ? rs.f : rs.d;
+  const int n_tiles = (N + CH_WG - 1) / CH_WG;
+  const int split = bid % g.splits;
+  bid /= g.splits;
+  const int tile = bid % n_tiles;
+  const int item_id = bid / n_tiles;
+  int expert, row0, rows;
+  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  const int k_begin = split * g.ksplit;
+  const int k_end = min(K, k_begin + g.ksplit);
+  if (k_begin >= k_end) return;
+  const int nks = (k_end - k_begin + 127) >> 7;       // K steps in this split
+  const int nch = (nks + C::PF - 1) / C::PF * C::PF;  // chunks (one K step each), a multiple of PF
+  const bool shared = expert >= rs.E;
+  const size_t ex = (size_t)(shared ? expert - rs.E : expert);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15, kg = lane >> 4;
+  uint8_t *const bufs[C::NBUF] = {b0, b1, b2, b3};
+
+  WOperands<NB, GATEUP, false> wo;
+  wo.init(g, shared, ex, tile * CH_WG + wave * CH_WAVE, k_begin, nks, lane);
+
+  v8i ring[C::PF][NB];
+  v4f acc[MSUB][NB];
+  int pass = 0;
+  for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
+    const int prow = min(C::MP, rows - p0);
+    const int msub = (prow + 15) >> 4;
+    float *rsc = row_scale + (pass & 1) * C::MP;
+    // This wave's two row groups (lane ln: row ln of each) and, for waves
+    // 0-3, 64 rows of the scale table; lookups issued together.
+    const uint8_t *abase[2];
+    {
+      int grow[2], sp[2];
 #pragma unroll
-      for (int cg = 0; cg < NB / 2; ++cg) {
-        if (ch[2 * cg] >= N) continue;
-        const float sgo = wsc[2 * cg], suo = wsc[2 * cg + 1];
-        float *hp = g.out + (size_t)(row0 + p0 + kg * 4) * N + ch[2 * cg];
-#pragma unroll
-        for (int m = 0; m < MSUB; ++m) {
-          if (m < msub) {
-            const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
-            const int rlim = prow - (m * 16 + kg * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float gv = acc[m][2 * cg][i] * sx4[i] * sgo;
-              const float uv = acc[m][2 * cg + 1][i] * sx4[i] * suo;
-              // SiLU(g)*u with the reciprocal instruction (1 ulp) for the
-              // divide
-              const float hv = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
-              if (m < msub - 1 || i < rlim) __builtin_nontemporal_store(hv, hp + (size_t)(m * 16 + i) * N);
-            }
-          }
-        }
+      for (int mm = 0; mm < 2; ++mm) {
+        grow[mm] = row0 + min(p0 + (2 * wave + mm) * 16 + ln, rows - 1);
+        sp[mm] = rs.sorted_pairs[min(grow[mm], rs.capacity - 1)];
       }
-    } else {
-      float *yp = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
+      const int trow = (wave & 3) * kWave + lane;
+      const int tgrow = row0 + min(p0 + trow, rows - 1);
+      const int tsp = rs.sorted_pairs[min(tgrow, rs.capacity - 1)];
 #pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        if (m < msub) {
-          const v4f sh4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
-          const int rlim = prow - (m * 16 + kg * 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (m < msub - 1 || i < rlim) {
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                if (ch[nb] < N)
-                  __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wsc[nb],
-                                              yp + (size_t)(m * 16 + i) * N + ch[nb]);
-            }
-          }
-        }
+      for (int mm = 0; mm < 2; ++mm) {
+        const int m = 2 * wave + mm;
+        const int a = act_row<GATEUP>(rs, grow[mm], sp[mm], m < msub && p0 + m * 16 + ln < rows);
+        abase[mm] = a < 0 ? nullptr : g.a + (size_t)a * K;
+      }
+      if (wave < 4) {
+        const int a = act_row<GATEUP>(rs, tgrow, tsp, trow < prow);
+        const float *src = a < 0 ? reinterpret_cast<const float *>(g_zero_piece) : g.a_scale + a;
+        dma_lds4(src, rsc + wave * kWave);
       }
     }
+    // Gather chunk c (K step c of the split) of this wave's row groups:
+    // fragment m of the chunk at m*2048, its two 64-byte K halves 1 KB apart.
+    auto gather = [&](int c, uint8_t *dst) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int kb = k_begin + c * 128 + p * 64 + kg * 16;
+          const uint8_t *src = (abase[mm] && kb < k_end) ? abase[mm] + kb : g_zero_piece;
+          dma_lds16(src, dst + ((2 * wave + mm) * 2 + p) * 1024);
+        }
+      }
+    };
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[m][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+    // issue order: gather 0 | weights 0, gather 1 | weights 1, gather 2;
+    // then per step ks: weights ks+2, gather ks+3
+    gather(0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    wo.load(ring[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    gather(1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    wo.load(ring[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    gather(2, b2);
+    __builtin_amdgcn_sched_barrier(0);
+    // 16 loads after gather 0: chunk 0 (and the scale table before it) landed
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+
+    for (int ks0 = 0; ks0 < nch; ks0 += C::NBUF) {
+#pragma unroll
+      for (int j = 0; j < C::NBUF; ++j) {
+        const int ks = ks0 + j;  // ks % NBUF == j, ks % PF == j % PF
+        if (ks >= nch) break;
+        const int s = j % C::PF;
+        const uint8_t *fa = bufs[j] + lane * 16;
+        // row groups in batches of four: a batch's fragments are all read
+        // from LDS before its MFMAs
+#pragma unroll
+        for (int mb = 0; mb < MSUB; mb += 4) {
+          if (mb < msub) {
+            v8i a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const v4i a0 = *reinterpret_cast<const v4i *>(fa + (mb + j) * 2048);
+              const v4i a1 = *reinterpret_cast<const v4i *>(fa + (mb + j) * 2048 + 1024);
+              a[j] = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[mb + j][nb] = mfma_e4m3_16x16x128(a[j], ring[s][nb], acc[mb + j][nb]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wo.load(ring[s], ks + C::PF);
+        __builtin_amdgcn_sched_barrier(0);
+        // chunk ks+3 goes to the buffer of chunk ks-1, which every wave
+        // finished before the last barrier
+        gather(ks + 3, bufs[(j + 3) % C::NBUF]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < nch)  // 16 loads after this wave's gather of chunk ks+1
+          asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else  // end of the pass: nothing in flight into the ring
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    }
+    gemm_epilogue<MSUB, NB, GATEUP, false>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
   }
 }
 

@@ -75,13 +75,16 @@ int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int
                        int32_t row_chunk);
 
 // waves: compute waves per workgroup of the grouped GEMMs (1..8; with up to
-// five, two workgroups share a CU).
+// five, two workgroups share a CU).  With 256-row passes (msub 16), waves ==
+// kPfWaves selects the prefill kernel (every wave gathers and computes),
+// any other count the loader-wave kernel with that many computing waves.
 constexpr int kGemmMaxWaves = 8;
 constexpr int kGemmMaxThreads = (kGemmMaxWaves + 1) * 64;
 // 256-row passes (msub 16, two loader waves) and four weight operands per
 // wave (nb 4) use up to 256 VGPRs: at most eight waves per workgroup.
 constexpr int kGemmMaxThreadsWide = 8 * 64;
 constexpr int kGemmMaxWaves16 = 6;
+constexpr int kPfWaves = 8;  // prefill GEMM: 256-row passes, every wave gathers and computes
 // msub_big > msub (nb 2, msub_big <= 8): items longer than 16*msub rows run
 // 16*msub_big-row passes in the same launch (items are cut at 16*msub_big).
 // stream_weights (nb 2, msub <= 8): the weight loads carry the non-temporal

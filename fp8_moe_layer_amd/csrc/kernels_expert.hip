@@ -51,6 +51,18 @@ __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMax
   wsgemm_tile<MSUB, NB, GATEUP, NT>(g, blockIdx.x, abuf);
 }
 
+// Prefill-sized batches: 256-row passes, eight waves that all gather and
+// compute (one workgroup per CU: 130 KB of LDS).
+template <bool GATEUP>
+__global__ __launch_bounds__(kPfWaves * 64) void pfgemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[PfChunk::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[PfChunk::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[PfChunk::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b3[PfChunk::BYTES];
+  __shared__ __attribute__((aligned(16))) float table[PfChunk::TABLE];
+  pf_tile<GATEUP>(g, blockIdx.x, b0, b1, b2, b3, table);
+}
+
 // Two row-pass shapes in one launch.  Work items are cut at 16*ML rows; an
 // item of at most 16*MS rows runs the MS shape (deeper weight prefetch, K
 // steps batched per LDS chunk), a longer one the ML shape.  Routing that
@@ -199,6 +211,17 @@ static hipError_t launch_ws(const GemmArgs &g, int waves, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool GATEUP>
+static hipError_t launch_pf(const GemmArgs &g, hipStream_t stream) {
+  const int N = GATEUP ? g.rs.f : g.rs.d;
+  const int ch_wg = kPfWaves * (GATEUP ? 16 : 32);
+  const int n_tiles = (N + ch_wg - 1) / ch_wg;
+  const int blocks = grid_items(g.rs) * n_tiles * g.splits;
+  if (blocks == 0) return hipSuccess;
+  pfgemm_kernel<GATEUP><<<blocks, kPfWaves * 64, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
 template <int MS, int ML, bool GATEUP, bool NT>
 static hipError_t launch_ws2(const GemmArgs &g, int waves, hipStream_t stream) {
   const int N = GATEUP ? g.rs.f : g.rs.d;
@@ -243,7 +266,8 @@ hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx
                           const ExpertWeights &w, float *h, int32_t msub, int32_t msub_big,
                           int32_t waves, int32_t nb, bool stream_weights, hipStream_t stream) {
   GemmArgs g{rs, xq, sx, nullptr, w, h, 1, rs.d};
-  if (msub >= 16) return launch_ws<16, 2, true>(g, waves, stream);
+  if (msub >= 16)
+    return waves == kPfWaves ? launch_pf<true>(g, stream) : launch_ws<16, 2, true>(g, waves, stream);
   if (nb >= 4) {
     if (msub >= 8) return launch_ws<8, 4, true>(g, waves, stream);
     if (msub >= 4) return launch_ws<4, 4, true>(g, waves, stream);
@@ -304,7 +328,8 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
   // ksplit is a whole number of msub chunks, hence of msub_big chunks too
-  if (msub >= 16) return launch_ws<16, 2, false>(g, waves, stream);
+  if (msub >= 16)
+    return waves == kPfWaves ? launch_pf<false>(g, stream) : launch_ws<16, 2, false>(g, waves, stream);
   if (nb >= 4) {
     if (msub >= 8) return launch_ws<8, 4, false>(g, waves, stream);
     if (msub >= 4) return launch_ws<4, 4, false>(g, waves, stream);

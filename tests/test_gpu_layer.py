@@ -140,12 +140,14 @@ def test_persistent_single_launch_matches_staged(small):
     assert torch.equal(a, b) and torch.equal(b, b2)
 
 
-@pytest.mark.parametrize("msub,waves,nb", [(16, 6, 2), (16, 3, 2), (8, 8, 2), (8, 7, 2), (2, 5, 2),
-                                           (1, 1, 2), (8, 7, 4), (4, 5, 4), (2, 3, 4), (1, 6, 4)])
+@pytest.mark.parametrize("msub,waves,nb", [(16, 0, 2), (16, 6, 2), (16, 3, 2), (8, 8, 2), (8, 7, 2),
+                                           (2, 5, 2), (1, 1, 2), (8, 7, 4), (4, 5, 4), (2, 3, 4),
+                                           (1, 6, 4)])
 def test_gemm_geometry_overrides(small, msub, waves, nb, monkeypatch):
     """Every row-pass height, compute-wave count and operand count of the
     grouped GEMMs (tile-tuning overrides) gives the same parity, on every
-    token."""
+    token.  msub 16 without a wave count runs the prefill kernel (eight
+    waves that all gather and compute), with one the loader-wave kernel."""
     monkeypatch.setenv("FP8MOE_MSUB", str(msub))
     monkeypatch.setenv("FP8MOE_WAVES", str(waves))
     monkeypatch.setenv("FP8MOE_NB", str(nb))

@@ -227,12 +227,19 @@ def test_expert_products_integer_exact(T, d, f, E, k, S):
     np.testing.assert_array_equal(y[real], yo[real])
 
 
-@pytest.mark.parametrize("name", ["tiny", "shared", "elastic"])
+@pytest.mark.parametrize("name", ["tiny", "shared", "elastic", "tall"])
 @pytest.mark.parametrize("no_requant", [False, True])
-def test_expert_stages_random(name, no_requant):
+def test_expert_stages_random(name, no_requant, monkeypatch):
     spec = {"tiny": wl.TINY,
             "shared": wl.TINY.with_(T=33, d=256, f=192, E=6, k=3, n_shared=2),
-            "elastic": wl.TINY.with_(T=50, d=128, f=320, E=32, k=8, k_choices=(1, 2, 4, 8))}[name]
+            "elastic": wl.TINY.with_(T=50, d=128, f=320, E=32, k=8, k_choices=(1, 2, 4, 8)),
+            # 256-row passes (prefill kernel): experts of about 300 rows and
+            # a shared expert of 600 take two and three passes; K tails of 64
+            # bytes (d = 704: 6 steps, f = 448: 4 steps); partial last
+            # channel tiles
+            "tall": wl.TINY.with_(T=600, d=704, f=448, E=4, k=2, n_shared=1)}[name]
+    if name == "tall":
+        monkeypatch.setenv("FP8MOE_MSUB", "16")
     m = lib()
     L = Layer(spec)
     bm = 16
