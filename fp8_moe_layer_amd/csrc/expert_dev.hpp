@@ -458,56 +458,30 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
 
 // ------------------------------------------------------------------ prefill grouped GEMM
 // Row passes of 256 rows (prefill-sized batches re-read an expert's weights
-// once per pass, so passes are as tall as LDS allows).  Eight waves, two per
-// SIMD, and every wave both gathers and computes: wave w gathers row groups
-// 2w and 2w+1 of each chunk (four direct-to-LDS loads) and computes 16
-// gate/up channels (32 down channels) over all 256 rows.  A split into
-// loader and compute waves left two SIMDs with one computing wave each.
+// once per pass, so passes are as tall as registers allow).  Eight waves,
+// two per SIMD, and every wave both gathers and computes: wave w gathers row
+// groups 2w and 2w+1 of each chunk and computes 16 gate/up channels (32
+// down channels) over all 256 rows.  A split into loader and compute waves
+// left two SIMDs with one computing wave each.
 //
-// Per K step every wave issues its loads in one fixed order, gather of chunk
-// ks+3 then weights of step ks+2, with scheduling fences between them, so
-// the number of loads issued after a given chunk's gather is a constant:
-// vmcnt(16) before the end-of-step barrier means this wave's part of chunk
-// ks+1 has landed, and after the barrier every wave's part has.  Gathers
-// past the last chunk read the zero piece into the buffer just freed, which
-// keeps that count constant to the end of the pass.
-//
-// The gathers are issued in inline assembly (dma_lds16/dma_lds4 below): the
-// compiler's wait-count pass, when it sees direct-to-LDS loads in a wave
-// that also reads LDS, waits for every outstanding load before the LDS
-// reads, which empties the gather pipeline every step.  Invisible to it,
-// they only make its waits for the weight registers stricter than needed
-// (those waits then also cover the gather issued two steps earlier).  The
-// four ring buffers are separate LDS arrays, the K loop unrolled by four.
+// A chunk is one K step (128 bytes) of the pass's 256 rows, 32 KB of LDS.
+// The gather goes through registers: chunk c is loaded at step c-3 into one
+// of two staging sets and written to LDS during step c-1, between MFMA
+// batches, into the buffer of chunk c-2 (two buffers).  Every load is an
+// ordinary one, so the compiler's wait counts stay exact (direct-to-LDS
+// loads make it wait for all outstanding loads before the LDS reads).  One
+// barrier per step: each wave's LDS writes of chunk t+1 are done, and every
+// wave finished chunk t-1, whose buffer the next writes reuse.
 struct PfChunk {
   static constexpr int MSUB = 16;
-  static constexpr int MP = 16 * MSUB;  // rows per pass
+  static constexpr int MP = 16 * MSUB;    // rows per pass
   static constexpr int BYTES = MP * 128;  // one K step of the pass's rows: 32 KB
-  static constexpr int NBUF = 4;          // LDS ring; gathers run three chunks ahead
   static constexpr int PF = 2;            // weight prefetch depth in K steps
-  static constexpr int TABLE = 2 * MP;    // scale table floats, one copy per pass parity
+  static constexpr int LDS = 2 * BYTES + 2 * MP * (int)sizeof(float);  // + scale table per pass parity
 };
 
-// Direct-to-LDS loads in inline assembly: 16 bytes per lane to lds + 16*lane
-// (dma_lds16) or 4 bytes to lds + 4*lane (dma_lds4); lds is a wave-uniform
-// LDS address.  The caller waits for them with s_waitcnt vmcnt.  They set
-// M0 themselves, so code using them must issue no other direct-to-LDS load
-// (the compiler keeps no value in M0 across them otherwise: M0 is written
-// right before each of its own uses).
-__device__ __forceinline__ void dma_lds16(const void *src, void *lds) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(a)
-               : "memory");
-}
-__device__ __forceinline__ void dma_lds4(const void *src, void *lds) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(a)
-               : "memory");
-}
-
 template <bool GATEUP>
-__device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *b0, uint8_t *b1,
-                                        uint8_t *b2, uint8_t *b3, float *row_scale) {
+__device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *abuf) {
   using C = PfChunk;
   constexpr int MSUB = C::MSUB, NB = 2, NW = kPfWaves;
   constexpr int CH_WAVE = GATEUP ? 16 : 32;
@@ -532,13 +506,14 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *b0,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, kg = lane >> 4;
-  uint8_t *const bufs[C::NBUF] = {b0, b1, b2, b3};
+  float *row_scale = reinterpret_cast<float *>(abuf + 2 * C::BYTES);
 
   WOperands<NB, GATEUP, false> wo;
   wo.init(g, shared, ex, tile * CH_WG + wave * CH_WAVE, k_begin, nks, lane);
 
   v8i ring[C::PF][NB];
   v4f acc[MSUB][NB];
+  v4i stage[2][4];  // gathered pieces of two chunks: (row group mm, K half p) at 2*mm + p
   int pass = 0;
   for (int p0 = 0; p0 < rows; p0 += C::MP, ++pass) {
     const int prow = min(C::MP, rows - p0);
@@ -547,6 +522,7 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *b0,
     // This wave's two row groups (lane ln: row ln of each) and, for waves
     // 0-3, 64 rows of the scale table; lookups issued together.
     const uint8_t *abase[2];
+    float tscale = 0.0f;
     {
       int grow[2], sp[2];
 #pragma unroll
@@ -563,53 +539,54 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *b0,
         const int a = act_row<GATEUP>(rs, grow[mm], sp[mm], m < msub && p0 + m * 16 + ln < rows);
         abase[mm] = a < 0 ? nullptr : g.a + (size_t)a * K;
       }
-      if (wave < 4) {
-        const int a = act_row<GATEUP>(rs, tgrow, tsp, trow < prow);
-        const float *src = a < 0 ? reinterpret_cast<const float *>(g_zero_piece) : g.a_scale + a;
-        dma_lds4(src, rsc + wave * kWave);
-      }
+      const int a = act_row<GATEUP>(rs, tgrow, tsp, trow < prow);
+      if (wave < 4 && a >= 0) tscale = g.a_scale[a];
     }
-    // Gather chunk c (K step c of the split) of this wave's row groups:
-    // fragment m of the chunk at m*2048, its two 64-byte K halves 1 KB apart.
-    auto gather = [&](int c, uint8_t *dst) {
+    // Chunk c of this wave's row groups: 16 bytes per lane and piece (row
+    // ln, K bytes kg*16 of each 64-byte half); zero past K or for padding.
+    auto gather = [&](int c, v4i (&st)[4]) {
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int kb = k_begin + c * 128 + p * 64 + kg * 16;
           const uint8_t *src = (abase[mm] && kb < k_end) ? abase[mm] + kb : g_zero_piece;
-          dma_lds16(src, dst + ((2 * wave + mm) * 2 + p) * 1024);
+          st[2 * mm + p] = load16(src);
         }
       }
+    };
+    // ... written where the MFMA reads expect it: fragment m of the chunk
+    // at m*2048, its two K halves 1 KB apart, lane l at l*16.
+    auto put = [&](int c, const v4i (&st)[4]) {
+      uint8_t *dst = abuf + (c & 1) * C::BYTES + lane * 16;
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          *reinterpret_cast<v4i *>(dst + ((2 * wave + mm) * 2 + p) * 1024) = st[2 * mm + p];
     };
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[m][nb] = v4f{0.f, 0.f, 0.f, 0.f};
-    // issue order: gather 0 | weights 0, gather 1 | weights 1, gather 2;
-    // then per step ks: weights ks+2, gather ks+3
-    gather(0, b0);
-    __builtin_amdgcn_sched_barrier(0);
+    // chunks 0 and 1 (and 2) gathered, chunk 0 written; weights of steps 0, 1
+    gather(0, stage[0]);
+    gather(1, stage[1]);
     wo.load(ring[0], 0);
-    __builtin_amdgcn_sched_barrier(0);
-    gather(1, b1);
-    __builtin_amdgcn_sched_barrier(0);
     wo.load(ring[1], 1);
-    __builtin_amdgcn_sched_barrier(0);
-    gather(2, b2);
-    __builtin_amdgcn_sched_barrier(0);
-    // 16 loads after gather 0: chunk 0 (and the scale table before it) landed
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    put(0, stage[0]);
+    gather(2, stage[0]);
+    if (wave < 4) rsc[(wave & 3) * kWave + lane] = tscale;
+    barrier_lds();
 
-    for (int ks0 = 0; ks0 < nch; ks0 += C::NBUF) {
+    for (int ks0 = 0; ks0 < nch; ks0 += C::PF) {
 #pragma unroll
-      for (int j = 0; j < C::NBUF; ++j) {
-        const int ks = ks0 + j;  // ks % NBUF == j, ks % PF == j % PF
-        if (ks >= nch) break;
-        const int s = j % C::PF;
-        const uint8_t *fa = bufs[j] + lane * 16;
+      for (int s = 0; s < C::PF; ++s) {
+        const int ks = ks0 + s;  // stage[(ks + 1) & 1] holds chunk ks+1
+        const uint8_t *fa = abuf + (ks & 1) * C::BYTES + lane * 16;
         // row groups in batches of four: a batch's fragments are all read
-        // from LDS before its MFMAs
+        // from LDS before its MFMAs; chunk ks+1 is written to LDS and chunk
+        // ks+3 gathered between batches
 #pragma unroll
         for (int mb = 0; mb < MSUB; mb += 4) {
           if (mb < msub) {
@@ -627,18 +604,13 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *b0,
               for (int nb = 0; nb < NB; ++nb)
                 acc[mb + j][nb] = mfma_e4m3_16x16x128(a[j], ring[s][nb], acc[mb + j][nb]);
           }
+          __builtin_amdgcn_sched_barrier(0);
+          if (mb == 4) put(ks + 1, stage[(ks + 1) & 1]);
+          if (mb == 8) gather(ks + 3, stage[(ks + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
         wo.load(ring[s], ks + C::PF);
-        __builtin_amdgcn_sched_barrier(0);
-        // chunk ks+3 goes to the buffer of chunk ks-1, which every wave
-        // finished before the last barrier
-        gather(ks + 3, bufs[(j + 3) % C::NBUF]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + 1 < nch)  // 16 loads after this wave's gather of chunk ks+1
-          asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else  // end of the pass: nothing in flight into the ring
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        barrier_lds();
       }
     }
     gemm_epilogue<MSUB, NB, GATEUP, false>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);

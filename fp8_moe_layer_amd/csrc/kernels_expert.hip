@@ -52,15 +52,27 @@ __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMax
 }
 
 // Prefill-sized batches: 256-row passes, eight waves that all gather and
-// compute (one workgroup per CU: 130 KB of LDS).
+// compute (one workgroup per CU: 256 VGPRs per wave, 66 KB of LDS).
+// Workgroups are dealt to the eight XCDs in turn (workgroup i to XCD i % 8),
+// and each XCD has its own L2: workgroup i takes the (item, tile) of its
+// XCD's contiguous share of the blocks that have work, so an XCD runs the
+// channel tiles of the same items (same activation rows) and the passes of
+// the same expert (same weight tiles) side by side.  Measured at a
+// 65536-row batch: L2 misses of the gate/up GEMM 2.4 GB -> 1.0 GB.
 template <bool GATEUP>
 __global__ __launch_bounds__(kPfWaves * 64) void pfgemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[PfChunk::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t b1[PfChunk::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t b2[PfChunk::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t b3[PfChunk::BYTES];
-  __shared__ __attribute__((aligned(16))) float table[PfChunk::TABLE];
-  pf_tile<GATEUP>(g, blockIdx.x, b0, b1, b2, b3, table);
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[PfChunk::LDS];
+  int bid = blockIdx.x;
+  if (g.rs.items) {
+    const int N = GATEUP ? g.rs.f : g.rs.d;
+    const int ch_wg = kPfWaves * (GATEUP ? 16 : 32);
+    const int n_real = *g.rs.n_items * ((N + ch_wg - 1) / ch_wg) * g.splits;
+    if (bid < n_real) {
+      const int q = n_real >> 3, r = n_real & 7, x = bid & 7, j = bid >> 3;
+      bid = x * q + min(x, r) + j;  // XCD x: blocks [x*q + min(x, r), +q + (x < r))
+    }
+  }
+  pf_tile<GATEUP>(g, bid, abuf);
 }
 
 // Two row-pass shapes in one launch.  Work items are cut at 16*ML rows; an
