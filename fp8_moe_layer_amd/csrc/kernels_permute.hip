@@ -51,21 +51,39 @@ __global__ __launch_bounds__(1024) void permute_layout_kernel(
     int32_t *__restrict__ inv_pairs, int32_t *__restrict__ n_blocks, WorkItem *__restrict__ items,
     int32_t *__restrict__ n_items, int row_chunk, int T, int S) {
   __shared__ int tot[kMaxExperts], off[kMaxExperts + 1], item_off[kMaxExperts + 1];
+  __shared__ int part[1024];
   const int ns = permute_slices(P);
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    int run = 0;  // exclusive prefix over slices
-    for (int b = 0; b < ns; ++b) {
+  // Exclusive prefix over the slices of each expert's counts, G threads per
+  // expert: thread (g, e) sums the contiguous slices [s0, s1), the groups'
+  // sums are prefixed in LDS, then each thread writes its slices' prefixes.
+  // (One thread walking all slices waited one load latency per slice.)
+  const int G = 1024 / E;
+  const int per = (ns + G - 1) / G;
+  const int e = threadIdx.x % E, g = threadIdx.x / E;
+  const bool act = g < G;
+  const int s0 = min(ns, g * per), s1 = min(ns, g * per + per);
+  if (act) {
+    int sum = 0;
+#pragma unroll 4
+    for (int b = s0; b < s1; ++b) sum += inv_pairs[b * kSlice + e];
+    part[g * E + e] = sum;
+  }
+  __syncthreads();
+  if (act) {
+    int run = 0;
+    for (int h = 0; h < g; ++h) run += part[h * E + e];
+    for (int b = s0; b < s1; ++b) {
       const int c = inv_pairs[b * kSlice + e];
       inv_pairs[b * kSlice + e] = run;
       run += c;
     }
-    tot[e] = run;
+    if (g == G - 1) tot[e] = run;  // the last group ends at slice ns
   }
   __syncthreads();
   build_layout<1024>(tot, off, item_off, P, E, bm, capacity, sorted_pairs, expert_offsets,
                      block_expert, n_blocks, items, n_items, row_chunk, T, S);
-  for (int e = threadIdx.x; e < E; e += 1024)
-    for (int b = 0; b < ns; ++b) inv_pairs[b * kSlice + e] += off[e];  // first row of slice b
+  if (act)
+    for (int b = s0; b < s1; ++b) inv_pairs[b * kSlice + e] += off[e];  // first row of slice b
 }
 
 __global__ __launch_bounds__(kSliceWaves * kWave) void permute_scatter_kernel(
