@@ -176,6 +176,21 @@ struct WOperands {
 // expert row row0): gate/up writes h = SiLU(g)*u, the down projection its
 // split's y slab.  rsc: the pass's activation scale per row (0 for a
 // padding row) in LDS.
+// e^(-g) for the SiLU in a few instructions: 2^y with y = -g*log2(e)
+// rounded to fp32, times 2^r ~ 1 + r*ln 2 for the residual r (the product's
+// rounding error, recovered by an fma, plus the part of log2(e) below fp32),
+// so the result stays within a few ulp over the whole range.  v_exp_f32
+// gives +inf past 2^128 (the SiLU then gives 0) and 0 below the fp32 range
+// (SiLU(g) = g).
+__device__ __forceinline__ float exp_neg(float g) {
+  constexpr float kLog2e = 1.44269502f;       // log2(e) rounded to fp32
+  constexpr float kLog2eLo = 1.92596299e-8f;  // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147181f;
+  const float y = -g * kLog2e;
+  const float r = fmaf(-g, kLog2e, -y) + (-g) * kLog2eLo;
+  return __builtin_amdgcn_exp2f(y) * (1.0f + r * kLn2);
+}
+
 template <int MSUB, int NB, bool GATEUP, bool NT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc)[MSUB][NB],
                                               const WOperands<NB, GATEUP, NT> &wo, const float *rsc,
@@ -206,7 +221,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
             const float uv = acc[m][2 * cg + 1][i] * sx4[i] * suo;
             // SiLU(g)*u with the reciprocal instruction (1 ulp) for the
             // divide
-            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
+            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + exp_neg(gv)) * uv;
             if (m < msub - 1 || i < rlim) __builtin_nontemporal_store(hv, hp + (size_t)(m * 16 + i) * N);
           }
         }
