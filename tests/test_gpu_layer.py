@@ -155,6 +155,16 @@ def test_gemm_geometry_overrides(small, msub, waves, nb, monkeypatch):
     _check(small, no_requant=True)
 
 
+@pytest.mark.parametrize("msub,splits", [(16, 2), (16, 3), (4, 2), (4, 3)])
+def test_down_k_splits(small, msub, splits, monkeypatch):
+    """The down projection cut into K splits (partial sums in separate y
+    slabs, added in split order by the combine), on the prefill kernel
+    (msub 16) and a decode shape: the same parity on every token."""
+    monkeypatch.setenv("FP8MOE_MSUB", str(msub))
+    monkeypatch.setenv("FP8MOE_DOWN_SPLITS", str(splits))
+    _check(small)
+
+
 @pytest.mark.parametrize("ms,ml", [(1, 2), (1, 4), (1, 8), (2, 4), (2, 8), (4, 8)])
 def test_two_shape_gemm(small, ms, ml, monkeypatch):
     """Work items cut at 16*ml rows, the ones of at most 16*ms rows on the
