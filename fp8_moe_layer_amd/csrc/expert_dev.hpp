@@ -52,6 +52,11 @@ struct GemmArgs {
   float *out;            // h [rows][f] or y [splits][rows][d]
   int32_t splits;        // K splits (down only; partial sums go to separate y slabs)
   int32_t ksplit;        // bytes of K per split (multiple of the chunk size)
+  // Decode down projection: tile t of expert e starts its K loop at step
+  // ((t + 5e) * krot) % nks and wraps (0: no rotation).  When all of a
+  // launch's workgroups run in one round they otherwise walk their weight
+  // rows in step, every one at the same K offset at the same time.
+  int32_t krot = 0;
 };
 
 __device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, int &expert,
@@ -124,7 +129,8 @@ struct WOperands {
   const uint8_t *bw[NB];
   int ch[NB];
   float wsc[NB];
-  int nks;  // K steps of this split
+  int nks;      // K steps of this split
+  int rot = 0;  // logical step ks < nks reads physical step (ks + rot) % nks
 
   // c0: the wave's first output channel; k_begin: first K byte of the split.
   __device__ __forceinline__ void init(const GemmArgs &g, bool shared, size_t ex, int c0, int k_begin,
@@ -160,7 +166,7 @@ struct WOperands {
   // step is clamped to the last one (its activation pieces are zero); the
   // zero padding of a 64-byte tail step meets zero activation pieces.
   __device__ __forceinline__ void load(v8i (&b)[NB], int ks) const {
-    ks = min(ks, nks - 1);
+    ks = ks < nks ? (ks + rot >= nks ? ks + rot - nks : ks + rot) : nks - 1;
     const int o0 = ks * 2048;
     const int o1 = o0 + 1024;
 #pragma unroll
@@ -325,6 +331,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   // activation pieces by a repeat of the last weight step.
   const int nks_pf = (nks + C::PF - 1) / C::PF * C::PF;
   const int nchunks = (nks_pf + C::KSC - 1) / C::KSC;  // LDS chunks of KSC steps
+  const int krot = (!GATEUP && g.krot && nks > 1) ? ((tile + 5 * expert) * g.krot) % nks : 0;
 
   const bool shared = expert >= rs.E;
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
@@ -391,8 +398,10 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
           for (int s = 0; s < C::KSC; ++s) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const int kb = k_begin + (c * C::KSC + s) * 128 + p * 64 + kg * 16;
-              const uint8_t *src = (abase[mm] && kb < k_end) ? abase[mm] + kb : g_zero_piece;
+              const int lks = c * C::KSC + s;  // logical step; past nks: zeros
+              const int pks = lks + krot >= nks ? lks + krot - nks : lks + krot;
+              const int kb = k_begin + pks * 128 + p * 64 + kg * 16;
+              const uint8_t *src = (abase[mm] && lks < nks && kb < k_end) ? abase[mm] + kb : g_zero_piece;
               __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ((m * C::KSC + s) * 2 + p) * 1024),
                                                16, 0, 0);
             }
@@ -415,6 +424,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   // ---------------- compute waves
   WOperands<NB, GATEUP, NT> wo;
   wo.init(g, shared, ex, tile * CH_WG + wave * CH_WAVE, k_begin, nks, lane);
+  wo.rot = krot;
 
   v8i ring[C::PF][NB];
   v4f acc[MSUB][NB];

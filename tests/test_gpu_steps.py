@@ -227,7 +227,7 @@ def test_expert_products_integer_exact(T, d, f, E, k, S):
     np.testing.assert_array_equal(y[real], yo[real])
 
 
-@pytest.mark.parametrize("name", ["tiny", "shared", "elastic", "tall"])
+@pytest.mark.parametrize("name", ["tiny", "shared", "elastic", "tall", "tall8"])
 @pytest.mark.parametrize("no_requant", [False, True])
 def test_expert_stages_random(name, no_requant, monkeypatch):
     spec = {"tiny": wl.TINY,
@@ -237,9 +237,14 @@ def test_expert_stages_random(name, no_requant, monkeypatch):
             # a shared expert of 600 take two and three passes; K tails of 64
             # bytes (d = 704: 6 steps, f = 448: 4 steps); partial last
             # channel tiles
-            "tall": wl.TINY.with_(T=600, d=704, f=448, E=4, k=2, n_shared=1)}[name]
+            "tall": wl.TINY.with_(T=600, d=704, f=448, E=4, k=2, n_shared=1),
+            # 128-row passes: the down projection's K loop starts at a
+            # rotated step per tile and wraps
+            "tall8": wl.TINY.with_(T=600, d=704, f=448, E=4, k=2, n_shared=1)}[name]
     if name == "tall":
         monkeypatch.setenv("FP8MOE_MSUB", "16")
+    if name == "tall8":
+        monkeypatch.setenv("FP8MOE_MSUB", "8")
     m = lib()
     L = Layer(spec)
     bm = 16
