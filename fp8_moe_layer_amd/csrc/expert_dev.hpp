@@ -206,48 +206,83 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
   const int N = GATEUP ? rs.f : rs.d;
   const int kg = lane >> 4;
   // Lane (ln, kg) holds rows m*16 + kg*4 + i of channel wo.ch[nb].  Only the
-  // last row group of a pass can run past the item's rows; a padding row
-  // has scale 0 (and zero activations): 0 out.
-  // Stores are non-temporal: the output stream does not push the weight
-  // stream's neighbours (activation rows, tables) out of L2.
+  // last row group of a pass can run past the item's rows (a pass of
+  // 16*MSUB real rows takes the unmasked path); a padding row has scale 0
+  // (and zero activations): 0 out.  The store address advances by one row
+  // per element (no table of row offsets).  Stores are non-temporal: the
+  // output stream does not push the weight stream's neighbours (activation
+  // rows, tables) out of L2.
+  const bool full = prow == 16 * MSUB;
   if (GATEUP) {
 #pragma unroll
     for (int cg = 0; cg < NB / 2; ++cg) {
       if (wo.ch[2 * cg] >= N) continue;
       const float sgo = wo.wsc[2 * cg], suo = wo.wsc[2 * cg + 1];
       float *hp = g.out + (size_t)(row0 + p0 + kg * 4) * N + wo.ch[2 * cg];
+      auto h_of = [&](int m, int i, float sxr) {
+        const float gv = acc[m][2 * cg][i] * sxr * sgo;
+        const float uv = acc[m][2 * cg + 1][i] * sxr * suo;
+        // SiLU(g)*u with the reciprocal instruction (1 ulp) for the divide
+        return gv * __builtin_amdgcn_rcpf(1.0f + exp_neg(gv)) * uv;
+      };
+      if (full) {
 #pragma unroll
-      for (int m = 0; m < MSUB; ++m) {
-        if (m < msub) {
+        for (int m = 0; m < MSUB; ++m) {
           const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
-          const int rlim = prow - (m * 16 + kg * 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float gv = acc[m][2 * cg][i] * sx4[i] * sgo;
-            const float uv = acc[m][2 * cg + 1][i] * sx4[i] * suo;
-            // SiLU(g)*u with the reciprocal instruction (1 ulp) for the
-            // divide
-            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + exp_neg(gv)) * uv;
-            if (m < msub - 1 || i < rlim) __builtin_nontemporal_store(hv, hp + (size_t)(m * 16 + i) * N);
+            __builtin_nontemporal_store(h_of(m, i, sx4[i]), hp);
+            hp += i < 3 ? N : 13 * N;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m) {
+          if (m < msub) {
+            const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+            const int rlim = prow - (m * 16 + kg * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float hv = h_of(m, i, sx4[i]);
+              if (m < msub - 1 || i < rlim) __builtin_nontemporal_store(hv, hp);
+              hp += i < 3 ? N : 13 * N;
+            }
           }
         }
       }
     }
   } else {
     float *yp = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
+    // every lane's channels inside N (all but a partial last tile): no
+    // per-store channel mask
+    const bool live = __builtin_amdgcn_ballot_w64(wo.ch[NB - 1] >= N) == 0;
+    if (full && live) {
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      if (m < msub) {
+      for (int m = 0; m < MSUB; ++m) {
         const v4f sh4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
-        const int rlim = prow - (m * 16 + kg * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (m < msub - 1 || i < rlim) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              if (wo.ch[nb] < N)
-                __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wo.wsc[nb],
-                                            yp + (size_t)(m * 16 + i) * N + wo.ch[nb]);
+          for (int nb = 0; nb < NB; ++nb)
+            __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wo.wsc[nb], yp + wo.ch[nb]);
+          yp += i < 3 ? N : 13 * N;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) {
+        if (m < msub) {
+          const v4f sh4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+          const int rlim = prow - (m * 16 + kg * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (m < msub - 1 || i < rlim) {
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                if (wo.ch[nb] < N)
+                  __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wo.wsc[nb], yp + wo.ch[nb]);
+            }
+            yp += i < 3 ? N : 13 * N;
           }
         }
       }
