@@ -67,6 +67,8 @@ def test_quantize_rows_bit_exact(rows, cols):
 @pytest.mark.parametrize("T,d,E,bias", [(1, 4096, 8, False), (37, 2048, 128, True),
                                         (100, 256, 8, False), (16, 2048, 512, True),
                                         (5, 64, 3, True),
+                                        # more than 16 experts: K split over a workgroup's waves
+                                        (512, 2048, 64, True), (19, 320, 200, False),
                                         # batches past the per-(token, expert) kernel: tiled fp32 MFMA path
                                         (1000, 320, 100, True), (4096, 2048, 128, False),
                                         (1024, 2048, 512, True)])
@@ -81,7 +83,7 @@ def test_router_logits(T, d, E, bias):
     assert err < 1e-5, err
 
 
-@pytest.mark.parametrize("T,E", [(3, 16), (3000, 40)])
+@pytest.mark.parametrize("T,E", [(3, 16), (300, 40), (3000, 40)])
 def test_router_one_hot_exact(T, E):
     d = 256
     g = torch.Generator().manual_seed(3)
