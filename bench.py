@@ -67,6 +67,9 @@ def parse():
     p.add_argument("--group", action="store_true",
                    help="qwen3: decode batches of 64 from a pool of 512 tokens, in arrival order "
                         "and grouped by expert affinity (moe_group_tokens)")
+    p.add_argument("--tiers", action="store_true",
+                   help="prism: the elastic-k pool as one mixed-k batch and as quality-tier "
+                        "batches at one k each (moe_k_tiers)")
     p.add_argument("--graph", action="store_true",
                    help="also time the layer captured in a HIP graph (one graph per weight copy)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -424,6 +427,55 @@ def main():
             grouping.append(entry)
             log(f"grouping alpha={alpha}: {entry}")
 
+    # ---- elastic-k pool: one mixed-k batch vs quality-tier batches at one k each
+    tiers = None
+    if args.tiers and cfg == "prism":
+        tiers = []
+        kp = kpt_all[:T].cpu().numpy()
+        tlays = {}
+
+        def tlay(k):
+            if k not in tlays:
+                tlays[k] = fp8.MoELayer(dw, w_router, k, bias)
+            return tlays[k]
+
+        def time_runs(runs):
+            for i in range(max(1, args.warmup // len(runs))):
+                for lay_, xb, kb, ob in runs:
+                    lay_.forward(xb, k_per_token=kb, out=ob)
+            rounds = max(1, args.steps // len(runs))
+            ev = HipEvents(2)
+            torch.cuda.synchronize()
+            ev.record(0, sh)
+            for r in range(rounds):
+                for lay_, xb, kb, ob in runs:
+                    lay_.forward(xb, k_per_token=kb, out=ob)
+            ev.record(1, sh)
+            torch.cuda.synchronize()
+            ms_ = ev.elapsed_ms(0, 1) / rounds
+            ev.close()
+            return ms_
+
+        xm = x_all[:T].contiguous()
+        mixed_ms = time_runs([(tlay(spec.k), xm, kpt_all[:T].contiguous(),
+                               torch.empty((T, d), dtype=torch.float32, device=dev))])
+        budget_pairs = int(kp.sum())
+        for tb, ov in ((256, 0), (256, 4096), (128, 0), (128, 4096)):
+            order, start, bk = fp8.k_tiers(kp, tb, ov)
+            runs = []
+            for b in range(len(bk)):
+                idx = torch.as_tensor(order[start[b]:start[b + 1]], device=dev, dtype=torch.long)
+                runs.append((tlay(int(bk[b])), x_all[idx].contiguous(), None,
+                             torch.empty((len(idx), d), dtype=torch.float32, device=dev)))
+            served_pairs = int(sum(int(bk[b]) * int(start[b + 1] - start[b]) for b in range(len(bk))))
+            tms = time_runs(runs)
+            entry = {"pool": T, "batch": tb, "overhead_pairs": ov, "n_batches": len(bk),
+                     "over_service": round(served_pairs / budget_pairs, 4),
+                     "us_per_pool_tiered": round(tms * 1e3, 1),
+                     "us_per_pool_mixed": round(mixed_ms * 1e3, 1)}
+            tiers.append(entry)
+            log(f"tiers: {entry}")
+
     if args.zipf_sweep and cfg == "qwen3":
         zipf = []
         zcopies = []
@@ -546,6 +598,8 @@ def main():
         res["zipf_sweep"] = zipf
     if grouping is not None:
         res["grouping"] = grouping
+    if tiers is not None:
+        res["tiers"] = tiers
     print(json.dumps(res), flush=True)
 
 

@@ -71,6 +71,7 @@ _last_error = _sig("moe_last_error", C.c_char_p)
 _abi_version = _sig("moe_abi_version", _i32)
 _debug_stage_events = _sig("moe_debug_stage_events", _i32, C.POINTER(_vp), _i32)
 _group_tokens = _sig("moe_group_tokens", _i32, _vp, _i32, _i32, _i32, _i32, _vp)
+_k_tiers = _sig("moe_k_tiers", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 
 N_STAGE_EVENTS = 8
 STAGES = ("route", "topk", "permute", "gate_up", "requant", "down", "combine")
@@ -187,6 +188,27 @@ def group_tokens(topk_ids, E: int, batch: int):
     _check(_group_tokens(ids.ctypes.data if n else None, n, k, E, batch,
                          order.ctypes.data if n else None))
     return order
+
+
+def k_tiers(k_per_token, batch: int, overhead: int):
+    """Plan quality-tier batches of a pool by routing budget (moe_k_tiers;
+    host computation).  k_per_token: [n] int32 budgets (numpy or a torch
+    tensor, copied to the host).  Returns (order, batch_start, batch_k):
+    batch b is order[batch_start[b]:batch_start[b+1]], run at k batch_k[b]."""
+    import numpy as np
+    if isinstance(k_per_token, torch.Tensor):
+        k_per_token = k_per_token.detach().cpu().numpy()
+    kpt = np.ascontiguousarray(k_per_token, dtype=np.int32).reshape(-1)
+    n = kpt.size
+    order = np.empty(n, dtype=np.int32)
+    start = np.empty(n + 1, dtype=np.int32)
+    bk = np.empty(max(n, 1), dtype=np.int32)
+    nb = np.zeros(1, dtype=np.int32)
+    _check(_k_tiers(kpt.ctypes.data if n else None, n, batch, overhead,
+                    order.ctypes.data if n else None, start.ctypes.data,
+                    bk.ctypes.data if n else None, nb.ctypes.data))
+    m = int(nb[0])
+    return order, start[:m + 1].copy(), bk[:m].copy()
 
 
 def capacity(T: int, E: int, k_max: int, block_m: int) -> int:

@@ -251,6 +251,28 @@ moe_status moe_fused_forward(const moe_dims *dims /*host*/, const float *x, cons
 moe_status moe_group_tokens(const int32_t *ids /*host*/, int32_t n, int32_t k, int32_t E,
                             int32_t batch, int32_t *order /*host*/);
 
+/* Quality-tier batching by routing budget ("MoE-Prism: Disentangling
+ * Monolithic Experts …", section Méthodologie B, offline throughput-oriented
+ * mode: requests sorted by their k and grouped into tiers; a tier's residual
+ * batch is dispatched at once or merged into the next tier, which serves it at
+ * the larger k).  Plans the dispatch of a pool of n tokens with routing
+ * budgets k_per_token into batches of at most `batch` tokens, each run at one
+ * k: tiers in ascending k, tokens of a tier in ascending number, full batches
+ * cut from the front of the tier's pool.  A residual of r < batch tokens of
+ * tier k is merged into the next tier when r * k_next < overhead + r * k
+ * (`overhead`: the cost of one more batch, in (token, slot) pairs), otherwise
+ * dispatched as a short batch; a merged residual leads the next tier's pool,
+ * and the last tier's residual is always dispatched.  No token is served
+ * below its budget.  Deterministic.  HOST memory: k_per_token [n], each in
+ * [1, MOE_MAX_K]; out: order [n] (tokens in dispatch order), batch_start
+ * [n+1] (batch b is order[batch_start[b] .. batch_start[b+1])), batch_k [n]
+ * (the k batch b runs at), n_batches [1].  Synchronous, no device work.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (n < 0, batch < 1, overhead < 0, a
+ * budget outside [1, MOE_MAX_K]). */
+moe_status moe_k_tiers(const int32_t *k_per_token /*host*/, int32_t n, int32_t batch,
+                       int32_t overhead, int32_t *order /*host*/, int32_t *batch_start /*host*/,
+                       int32_t *batch_k /*host*/, int32_t *n_batches /*host*/);
+
 /* ------------------------------------------------------------------------ */
 
 /* Stage timing (instrumentation, not part of the layer).  After this call,

@@ -54,3 +54,34 @@ def distinct_per_batch(ids, order, batch: int) -> list:
     experts = token_experts(ids)
     return [len(set().union(*(experts[t] for t in order[b:b + batch])))
             for b in range(0, len(order), batch)]
+
+
+def k_tiers(k_per_token, batch: int, overhead: int):
+    """Quality-tier batches by routing budget -- "MoE-Prism: Disentangling
+    Monolithic Experts …", section Méthodologie B (offline, throughput-
+    oriented mode): sort the requests by k, group them into tiers, and either
+    dispatch a tier's residual batch at once or merge it into the next tier,
+    which serves it at that tier's larger k.
+
+    The package's reading of the pages' local throughput rule: r residual
+    tokens of tier k cost one batch overhead plus r*k pairs when dispatched
+    alone, and r*k_next pairs when merged; merging wins only when strictly
+    cheaper.  Returns a list of (k, [tokens]) batches in dispatch order."""
+    kpt = [int(v) for v in np.asarray(k_per_token).reshape(-1)]
+    levels = sorted(set(kpt))
+    batches = []
+    carried = []
+    for i, k in enumerate(levels):
+        pool = carried + [t for t in range(len(kpt)) if kpt[t] == k]
+        while len(pool) >= batch:
+            batches.append((k, pool[:batch]))
+            pool = pool[batch:]
+        carried = []
+        if not pool:
+            continue
+        r = len(pool)
+        if i + 1 < len(levels) and r * levels[i + 1] < overhead + r * k:
+            carried = pool
+        else:
+            batches.append((k, pool))
+    return batches
