@@ -147,12 +147,17 @@ def measured_peaks(torch, dev) -> dict:
             "copy_note": "1 GiB device copy, read + write bytes over time (torch copy kernel)"}
 
 
+# The sources that make the expert GEMM kernels and their launches: device
+# code, launchers and the host planner that picks their shapes.
+GEMM_SOURCES = ("abi.hip", "common.hpp", "expert_dev.hpp", "internal.hpp", "kernels_expert.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources, to tell whether stored counter readings still
-    describe the kernels being timed."""
+    """Hash of the expert GEMMs' sources, to tell whether stored counter
+    readings of the gate/up kernel still describe the kernel being timed."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_moe_layer_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMM_SOURCES:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
