@@ -575,6 +575,12 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
                         "route")))
       return s;
     mark(1);
+  } else if (!lg && route_tile_applies(dims->T, dims->E)) {
+    if ((s = hip_status(launch_route_prefill(x, w_router, router_bias, dims->T, dims->d, dims->E,
+                                             dims->k_max, k_per_token, logits, xq, sx, ids, tw, st),
+                        "route")))
+      return s;
+    mark(1);
   } else {
     if (!lg) {
       if ((s = hip_status(launch_route_logits(x, w_router, router_bias, dims->T, dims->d, dims->E,

@@ -73,20 +73,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(dpp_mov<CTRL>(__float_as_int(v)));
 }
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_mov(uint64_t v) {
-  const uint32_t lo = (uint32_t)dpp_mov<CTRL>((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)dpp_mov<CTRL>((int)(uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
 
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ uint64_t readlane(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
 }
 
 // Butterfly inside each row of 16 (every lane of a row ends with the row's
@@ -109,9 +99,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
-}
 
 // Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {

@@ -62,6 +62,13 @@ hipError_t launch_route_topk_fused(const float *x, const float *w_router, const 
                                    int32_t T, int32_t d, int32_t E, int32_t k_max,
                                    const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
                                    int32_t *ids, float *w, hipStream_t stream);
+// Prefill-sized batches with E <= 128 (route_tile_applies(T, E)): logits,
+// quantised x and top-k in one launch; the logits equal launch_router's.
+bool route_tile_applies(int32_t T, int32_t E);
+hipError_t launch_route_prefill(const float *x, const float *w_router, const float *bias,
+                                int32_t T, int32_t d, int32_t E, int32_t k_max,
+                                const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
+                                int32_t *ids, float *w, hipStream_t stream);
 hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
                        const int32_t *k_per_token, int32_t *ids, float *w, hipStream_t stream);
 // items/n_items/row_chunk: optional work list for the expert stages (row_chunk

@@ -140,6 +140,193 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const float *__restric
               lds + kRT * kRS);
 }
 
+// ------------------------------------------------------------------ routing, prefill-sized
+// Batches with many tokens and at most 128 experts: one workgroup of eight
+// waves takes TT = 2048/EW tokens against all experts (EW: E padded to 32, 64
+// or 128), so each wave owns one 16 x 16 logit tile on v_mfma_f32_16x16x4_f32
+// and every token is read by one workgroup only.  K advances 64 floats at a
+// time through two LDS buffers (one barrier per chunk), the next chunk's
+// global loads in flight while the current one is multiplied.  A lane reads
+// its fragments as four 16-byte pieces: lane (r, q) feeds k = 16q + s to MFMA
+// step s, the same k for both operands, so every product of the chunk is
+// summed once.  The loading threads keep each token row's |x| maximum on the
+// way; after the K loop the workgroup quantises its tokens (re-reading x) and,
+// from the logits it keeps in LDS, picks their top-k with softmax weights.
+// With xq == nullptr only the logits are written (moe_router_logits), with the
+// same arithmetic, so the two give the same logits bit for bit.
+constexpr int kRtChunk = 64, kRtStride = kRtChunk + 4, kRtThreads = 512, kRtPrefetch = 4;
+
+template <int EW>
+__global__ __launch_bounds__(kRtThreads) void route_tile_kernel(
+    const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
+    int T, int d, int E, int k_max, const int32_t *__restrict__ kpt, float *__restrict__ logits,
+    uint8_t *__restrict__ xq, float *__restrict__ sx, int32_t *__restrict__ ids,
+    float *__restrict__ w) {
+  constexpr int TT = 2048 / EW, TB = TT / 16;
+  constexpr int ROWS = TT + EW, NV = ROWS * 16, CJ = (NV + kRtThreads - 1) / kRtThreads;
+  constexpr int XJ = (TT * 16 + kRtThreads - 1) / kRtThreads;  // staging slots holding x
+  constexpr int PF = kRtPrefetch;
+  static_assert(TB * (EW / 16) == kRtThreads / kWave, "one 16x16 tile per wave");
+  __shared__ __attribute__((aligned(16))) float buf[2][ROWS * kRtStride];
+  __shared__ float ls[TT * EW];
+  __shared__ float ramax[TT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * TT;
+  const int tb = wave % TB, eb = wave / TB;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int nch = d / kRtChunk;
+
+  // Each thread's staging slots: a fixed source row (clamped into range, so
+  // every load is issued unconditionally and the wait counts stay exact) and
+  // whether the row is real; chunk ch reads columns ch*64 + c .. +3.
+  const float *src[CJ];
+  bool real[CJ];
+#pragma unroll
+  for (int j = 0; j < CJ; ++j) {
+    const int i = tid + j * kRtThreads, r = (i < NV ? i : NV - 1) >> 4, c = (i & 15) * 4;
+    if (r < TT) {
+      const int t = t0 + r;
+      real[j] = i < NV && t < T;
+      src[j] = x + (size_t)(t < T ? t : T - 1) * d + c;
+    } else {
+      const int e = r - TT;
+      real[j] = i < NV && e < E;
+      src[j] = wr + (size_t)(e < E ? e : E - 1) * d + c;
+    }
+  }
+  v4f stg[PF][CJ];
+  float amx[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) amx[j] = 0.0f;
+  auto fetch = [&](v4f (&st)[CJ], int ch) {
+    const int k0 = (ch < nch ? ch : nch - 1) * kRtChunk;  // past the end: reload the last chunk
+#pragma unroll
+    for (int j = 0; j < CJ; ++j) st[j] = *reinterpret_cast<const v4f *>(src[j] + k0);
+  };
+  auto put = [&](const v4f (&st)[CJ], float *b) {
+#pragma unroll
+    for (int j = 0; j < CJ; ++j) {
+      const int i = tid + j * kRtThreads;
+      const v4f v = real[j] ? st[j] : v4f{0.f, 0.f, 0.f, 0.f};
+      if (i < NV) *reinterpret_cast<v4f *>(b + (i >> 4) * kRtStride + (i & 15) * 4) = v;
+    }
+#pragma unroll
+    for (int j = 0; j < XJ; ++j)  // x rows come first: slots j < XJ
+      if (tid + j * kRtThreads < TT * 16)
+        amx[j] = fmaxf(amx[j], fmaxf(fmaxf(fabsf(st[j].x), fabsf(st[j].y)),
+                                     fmaxf(fabsf(st[j].z), fabsf(st[j].w))));
+  };
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  // chunk c is loaded into stg[c % PF] at step c - PF + 1 and written to LDS
+  // at the end of step c - 1
+#pragma unroll
+  for (int c = 0; c < PF - 1; ++c) fetch(stg[c], c);
+  put(stg[0], buf[0]);
+  __syncthreads();
+  for (int ch0 = 0; ch0 < nch; ch0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int ch = ch0 + s;
+      if (ch >= nch) break;
+      fetch(stg[(s + PF - 1) % PF], ch + PF - 1);
+      const float *b = buf[ch & 1];
+      const float *xa = b + (tb * 16 + lr) * kRtStride + 16 * lq;
+      const float *wb = b + (TT + eb * 16 + lr) * kRtStride + 16 * lq;
+      v4f xv[4], wv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[j] = *reinterpret_cast<const v4f *>(xa + 4 * j);
+        wv[j] = *reinterpret_cast<const v4f *>(wb + 4 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[j].x, wv[j].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[j].y, wv[j].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[j].z, wv[j].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[j].w, wv[j].w, acc, 0, 0, 0);
+      }
+      if (ch + 1 < nch) put(stg[(s + 1) % PF], buf[(ch + 1) & 1]);
+      __syncthreads();
+    }
+  }
+
+  // logits: tile rows are tokens, columns experts
+  const int e = eb * 16 + lr;
+  const float be = (bias && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tb * 16 + 4 * lq + i, t = t0 + r;
+    const float lg = bias ? acc[i] + be : acc[i];
+    ls[r * EW + e] = lg;
+    if (t < T && e < E) logits[(size_t)t * E + e] = lg;
+  }
+  if (!xq) return;
+  // each token row's |x| maximum: the 16 lanes that loaded it are one DPP row
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    float m = amx[j];
+    m = fmaxf(m, dpp_mov<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_mov<kDppQuadXor2>(m));
+    m = fmaxf(m, dpp_mov<kDppHalfMirror>(m));
+    m = fmaxf(m, dpp_mov<kDppMirror>(m));
+    const int i = tid + j * kRtThreads;
+    if (i < TT * 16 && (lane & 15) == 0) ramax[i >> 4] = m;
+  }
+  __syncthreads();
+  // a wave per token: quantise it (re-reading x), then its top-k from LDS
+  for (int r = wave; r < TT; r += kRtThreads / kWave) {
+    const int t = t0 + r;
+    if (t >= T) break;
+    const float m = ramax[r];
+    const float rq = m != 0.0f ? kE4m3Max / m : 1.0f;
+    const float *xr = x + (size_t)t * d;
+    uint8_t *q = xq + (size_t)t * d;
+    for (int i0 = 0; i0 < d; i0 += 4 * kWave * 4) {
+      v4f v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + (u * kWave + lane) * 4;
+        v[u] = i < d ? *reinterpret_cast<const v4f *>(xr + i) : v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + (u * kWave + lane) * 4;
+        if (i < d) *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v[u].x * rq, v[u].y * rq, v[u].z * rq, v[u].w * rq);
+      }
+    }
+    if (lane == 0) sx[t] = m != 0.0f ? m / kE4m3Max : 1.0f;
+    topk_row_wave(ls + r * EW, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+                  w + (size_t)t * k_max, lane);
+  }
+}
+
+// Prefill-sized batches route in one launch (logits, quantised x, top-k).
+bool route_tile_applies(int32_t T, int32_t E) {
+  return E <= 128 && (int64_t)T * E > kRouterDotMax;
+}
+
+static hipError_t launch_route_tile(const float *x, const float *w_router, const float *bias,
+                                    int32_t T, int32_t d, int32_t E, int32_t k_max,
+                                    const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
+                                    int32_t *ids, float *w, hipStream_t stream) {
+  if (E <= 32)
+    route_tile_kernel<32><<<(T + 63) / 64, kRtThreads, 0, stream>>>(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w);
+  else if (E <= 64)
+    route_tile_kernel<64><<<(T + 31) / 32, kRtThreads, 0, stream>>>(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w);
+  else
+    route_tile_kernel<128><<<(T + 15) / 16, kRtThreads, 0, stream>>>(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_prefill(const float *x, const float *w_router, const float *bias,
+                                int32_t T, int32_t d, int32_t E, int32_t k_max,
+                                const int32_t *kpt, float *logits, uint8_t *xq, float *sx,
+                                int32_t *ids, float *w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  return launch_route_tile(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w, stream);
+}
+
 hipError_t launch_route_logits(const float *x, const float *w_router, const float *bias, int32_t T,
                                int32_t d, int32_t E, float *logits, uint8_t *xq, float *sx,
                                hipStream_t stream) {
@@ -162,6 +349,9 @@ hipError_t launch_router(const float *x, const float *w_router, const float *bia
                                                            nullptr, nullptr);
     return hipGetLastError();
   }
+  if (route_tile_applies(T, E))  // the arithmetic of the fused prefill routing
+    return launch_route_tile(x, w_router, bias, T, d, E, 0, nullptr, logits, nullptr, nullptr,
+                             nullptr, nullptr, stream);
   dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
   router_mfma_kernel<<<grid, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits);
   return hipGetLastError();

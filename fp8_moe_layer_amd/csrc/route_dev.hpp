@@ -175,56 +175,64 @@ __device__ __forceinline__ void router_tile(const float *__restrict__ x,
 }
 
 // ------------------------------------------------------------------ top-k
-// One wave per token.  Each expert becomes a 64-bit key: the logit's bits
-// mapped to an unsigned order (with -0 folded onto +0) in the high word and
-// 0xFFFF - e in the low word, so the largest key is the largest logit with
-// the lowest index.  k_t rounds of a wave-wide max pick the slots in order;
-// the softmax over the picked logits is accumulated in slot order.
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
+// One wave per token.  Each expert's logit becomes an unsigned order key (its
+// bits mapped so that unsigned order is float order, -0 folded onto +0; 0 is
+// below every finite logit and marks a taken or absent expert).  k_t rounds
+// pick the slots in order: a wave-wide max of the keys gives the largest
+// logit, and a ballot of the lanes holding it gives the lowest expert index
+// among equals (expert e sits in lane e % 64, slot e / 64).  The softmax over
+// the picked logits is accumulated in slot order.
+__device__ __forceinline__ uint32_t order_key(float l) {
   uint32_t b = __float_as_uint(l);
   if ((b & 0x7fffffffu) == 0) b = 0;  // -0 == +0
-  uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFF - e);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// The logit a key was made from (-0 comes back as +0, which gives the same
-// exponentials below).
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
+// The logit an order key was made from (-0 comes back as +0, which gives the
+// same exponentials below).
+__device__ __forceinline__ float key_logit(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return (uint32_t)wave_reduce((int)v, [](int a, int b) {
+    return (uint32_t)a > (uint32_t)b ? a : b;
+  });
 }
 
 constexpr int kTopkSlots = kMaxExperts / kWave;
 
-// l: the token's E logits (global memory or LDS); writes the token's k_max
-// slots of ids / w.
-__device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, int kt,
-                                              int32_t *__restrict__ ids_row,
-                                              float *__restrict__ w_row, int lane) {
+// NS slots of 64 experts per lane (E <= 64 * NS).
+template <int NS>
+__device__ __forceinline__ void topk_row_wave_n(const float *l, int E, int k_max, int kt,
+                                                int32_t *__restrict__ ids_row,
+                                                float *__restrict__ w_row, int lane) {
   // every slot's logit is requested before any is used (one memory latency)
-  float lv[kTopkSlots];
+  float lv[NS];
 #pragma unroll
-  for (int c = 0; c < kTopkSlots; ++c) {
+  for (int c = 0; c < NS; ++c) {
     const int e = lane + c * kWave;
     lv[c] = c * kWave < E ? l[e < E ? e : E - 1] : 0.0f;
   }
-  uint64_t key[kTopkSlots];
+  uint32_t key[NS];
 #pragma unroll
-  for (int c = 0; c < kTopkSlots; ++c) {
-    const int e = lane + c * kWave;
-    key[c] = e < E ? route_key(lv[c], e) : 0ull;
-  }
+  for (int c = 0; c < NS; ++c) key[c] = lane + c * kWave < E ? order_key(lv[c]) : 0u;
   float m = 0.0f, z = 0.0f, my_eps = 0.0f;
   int my_id = -1;
   for (int j = 0; j < kt; ++j) {
-    uint64_t best = 0;
+    uint32_t best = key[0];
 #pragma unroll
-    for (int c = 0; c < kTopkSlots; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_u64(best);
-    const int e = 0xFFFF - (int)(best & 0xFFFFu);
-    const float lv = key_logit(best);  // no dependent memory read per round
-    if (j == 0) m = lv;
-    const float eps = expf(lv - m);
+    for (int c = 1; c < NS; ++c) best = key[c] > best ? key[c] : best;
+    best = wave_max_u32(best);
+    int e = -1;
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {  // the lowest slot, then the lowest lane, holding the max
+      const uint64_t hold = __ballot(key[c] == best);
+      if (e < 0 && hold) e = c * kWave + (int)__builtin_ctzll(hold);
+    }
+    const float lg = key_logit(best);  // no dependent memory read per round
+    if (j == 0) m = lg;
+    const float eps = expf(lg - m);
     z += eps;
     if (lane == j) {
       my_eps = eps;
@@ -232,14 +240,27 @@ __device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, 
     }
     if ((e & 63) == lane) {
 #pragma unroll
-      for (int c = 0; c < kTopkSlots; ++c)
-        if (c == (e >> 6)) key[c] = 0ull;
+      for (int c = 0; c < NS; ++c)
+        if (c == (e >> 6)) key[c] = 0u;
     }
   }
   if (lane < k_max) {
     ids_row[lane] = lane < kt ? my_id : -1;
     w_row[lane] = lane < kt ? my_eps / z : 0.0f;
   }
+}
+
+// l: the token's E logits (global memory or LDS); writes the token's k_max
+// slots of ids / w.
+__device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, int kt,
+                                              int32_t *__restrict__ ids_row,
+                                              float *__restrict__ w_row, int lane) {
+  if (E <= kWave)
+    topk_row_wave_n<1>(l, E, k_max, kt, ids_row, w_row, lane);
+  else if (E <= 2 * kWave)
+    topk_row_wave_n<2>(l, E, k_max, kt, ids_row, w_row, lane);
+  else
+    topk_row_wave_n<kTopkSlots>(l, E, k_max, kt, ids_row, w_row, lane);
 }
 
 __device__ __forceinline__ void topk_token_wave(const float *__restrict__ logits, int T, int E,

@@ -71,6 +71,7 @@ def test_quantize_rows_bit_exact(rows, cols):
                                         (512, 2048, 64, True), (19, 320, 200, False),
                                         # batches past the per-(token, expert) kernel: tiled fp32 MFMA path
                                         (1000, 320, 100, True), (4096, 2048, 128, False),
+                                        (2100, 192, 32, True), (1100, 256, 64, True),
                                         (1024, 2048, 512, True)])
 def test_router_logits(T, d, E, bias):
     g = torch.Generator().manual_seed(T + d + E)
@@ -94,6 +95,33 @@ def test_router_one_hot_exact(T, E):
     x[torch.arange(T), cols] = 1.0
     lg = to_np(lib().router_logits(x.to(dev()), wr.to(dev()), b.to(dev())))
     np.testing.assert_array_equal(lg, (wr[:, cols].T + b).numpy())
+
+
+@pytest.mark.parametrize("T,d,E,k,var", [(1100, 256, 64, 6, False), (700, 320, 100, 8, True),
+                                         (2100, 192, 32, 4, True), (4096, 2048, 128, 8, False)])
+def test_prefill_routing_equals_steps(T, d, E, k, var):
+    """Past the per-(token, expert) kernels the layer routes in one launch
+    (logits, quantised x, top-k): its ids and weights equal, bit for bit, those
+    of moe_route_topk on moe_router_logits' logits, and the layer's output
+    matches the oracle run on those logits."""
+    m = lib()
+    spec = wl.TINY.with_(T=T, d=d, f=128, E=E, k=k, bias="zipf", bias_param=1.0,
+                         k_choices=tuple(range(1, k + 1)) if var else ())
+    L = Layer(spec)
+    kpt = L.kpt
+    lg = m.router_logits(L.x, L.w_router, L.bias)
+    ids_s, w_s = m.route_topk(lg, k, kpt)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev())
+    w = torch.empty((T, k), dtype=torch.float32, device=dev())
+    out = L.layer().forward(L.x, k_per_token=kpt, topk_ids=ids, topk_w=w)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_s)
+    assert torch.equal(w, w_s)
+    rows = np.unique(np.random.default_rng(T).choice(T, 256, replace=False))
+    ref, _, _ = oracle.forward(to_np(L.x)[rows], L.qw, k, logits_override=to_np(lg)[rows],
+                               k_per_token=None if kpt is None else to_np(kpt)[rows])
+    err = rel_l2(to_np(out)[rows], ref)
+    assert err <= 2e-2, err
 
 
 # ----------------------------------------------------------------- top-k
