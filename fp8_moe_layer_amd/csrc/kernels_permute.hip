@@ -45,6 +45,8 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_count_kernel(
   }
 }
 
+constexpr int kLayoutRegSlices = 16;  // slices per thread held in registers
+
 __global__ __launch_bounds__(1024) void permute_layout_kernel(
     int P, int E, int bm, int capacity, int32_t *__restrict__ sorted_pairs,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ block_expert,
@@ -62,6 +64,36 @@ __global__ __launch_bounds__(1024) void permute_layout_kernel(
   const int e = threadIdx.x % E, g = threadIdx.x / E;
   const bool act = g < G;
   const int s0 = min(ns, g * per), s1 = min(ns, g * per + per);
+  if (per <= kLayoutRegSlices) {
+    // the thread's slice counts stay in registers: one read of them, and one
+    // write of the slices' first rows once the segment offsets are known
+    int c[kLayoutRegSlices];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kLayoutRegSlices; ++j) {
+      c[j] = act && s0 + j < s1 ? inv_pairs[(s0 + j) * kSlice + e] : 0;
+      sum += c[j];
+    }
+    if (act) part[g * E + e] = sum;
+    __syncthreads();
+    int run = 0;
+    if (act) {
+      for (int h = 0; h < g; ++h) run += part[h * E + e];
+      if (g == G - 1) tot[e] = run + sum;  // the last group ends at slice ns
+    }
+    __syncthreads();
+    build_layout<1024>(tot, off, item_off, P, E, bm, capacity, sorted_pairs, expert_offsets,
+                       block_expert, n_blocks, items, n_items, row_chunk, T, S);
+    if (act) {
+      run += off[e];
+#pragma unroll
+      for (int j = 0; j < kLayoutRegSlices; ++j) {
+        if (s0 + j < s1) inv_pairs[(s0 + j) * kSlice + e] = run;  // first row of slice s0 + j
+        run += c[j];
+      }
+    }
+    return;
+  }
   if (act) {
     int sum = 0;
 #pragma unroll 4

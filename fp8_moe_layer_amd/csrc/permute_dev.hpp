@@ -162,10 +162,20 @@ __device__ __forceinline__ void build_layout(const int *tot, int *off, int *item
   const int nb_cap = (capacity + bm - 1) / bm;
   for (int e = tid; e <= E; e += NT) expert_offsets[e] = off[e];
   if (tid == 0) *n_blocks = nb;
-  for (int e = tid; e < E; e += NT) {
-    for (int b = off[e] / bm; b < off[e + 1] / bm; ++b) block_expert[b] = e;
-    for (int r = off[e] + tot[e]; r < off[e + 1]; ++r) sorted_pairs[r] = sentinel;
+  // a thread per block: its expert is the last segment starting at or before
+  // it (off is non-decreasing; empty segments start where the next one does)
+  for (int b = tid; b < nb; b += NT) {
+    const int row = b * bm;
+    int lo = 0, hi = E - 1;  // off[lo] <= row < off[E]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    block_expert[b] = lo;
   }
+  for (int e = tid; e < E; e += NT)
+    for (int r = off[e] + tot[e]; r < off[e + 1]; ++r) sorted_pairs[r] = sentinel;
   for (int b = nb + tid; b < nb_cap; b += NT) block_expert[b] = -1;
   for (int r = total + tid; r < capacity; r += NT) sorted_pairs[r] = sentinel;
 
