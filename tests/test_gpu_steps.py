@@ -72,6 +72,10 @@ def test_quantize_rows_bit_exact(rows, cols):
                                         # batches past the per-(token, expert) kernel: tiled fp32 MFMA path
                                         (1000, 320, 100, True), (4096, 2048, 128, False),
                                         (2100, 192, 32, True), (1100, 256, 64, True),
+                                        # one K chunk (fewer than the prefetch depth), three
+                                        # chunks, expert counts that pad the tile
+                                        (1100, 64, 64, False), (3000, 192, 40, True),
+                                        (3900, 128, 17, True), (2000, 320, 33, False),
                                         (1024, 2048, 512, True)])
 def test_router_logits(T, d, E, bias):
     g = torch.Generator().manual_seed(T + d + E)
@@ -98,7 +102,8 @@ def test_router_one_hot_exact(T, E):
 
 
 @pytest.mark.parametrize("T,d,E,k,var", [(1100, 256, 64, 6, False), (700, 320, 100, 8, True),
-                                         (2100, 192, 32, 4, True), (4096, 2048, 128, 8, False)])
+                                         (2100, 192, 32, 4, True), (4096, 2048, 128, 8, False),
+                                         (1100, 64, 64, 6, True), (3900, 128, 17, 17, False)])
 def test_prefill_routing_equals_steps(T, d, E, k, var):
     """Past the per-(token, expert) kernels the layer routes in one launch
     (logits, quantised x, top-k): its ids and weights equal, bit for bit, those
