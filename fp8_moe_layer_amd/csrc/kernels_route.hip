@@ -41,6 +41,94 @@ hipError_t launch_quantize_rows(const float *x, int32_t rows, int32_t cols, uint
 }
 
 // ------------------------------------------------------------------ router
+// Batches of up to 65536 (token, expert) pairs: a wave takes two tokens x
+// four experts and forms each of its eight dot products exactly as
+// router_dot_wave does (the same lanes, the same order of FMAs, the same wave
+// sum, the parts added in order), so the logits are the same bit for bit, while
+// each x and W_r row is read once per wave instead of once per product.  The
+// wave of the first four experts also quantises its tokens.
+constexpr int kDotTok = 2, kDotExp = 4;
+constexpr int64_t kRouterDotTileMin = 16384;  // (token, expert) pairs: from here the tiled form
+
+__global__ __launch_bounds__(256) void router_dot_tile_kernel(const float *__restrict__ x,
+                                                              const float *__restrict__ wr,
+                                                              const float *__restrict__ bias, int T,
+                                                              int d, int E,
+                                                              float *__restrict__ logits,
+                                                              uint8_t *__restrict__ xq,
+                                                              float *__restrict__ sx) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n_eq = (E + kDotExp - 1) / kDotExp;
+  const int tp = wid / n_eq, eq = wid - tp * n_eq;
+  const int t0 = tp * kDotTok, e0 = eq * kDotExp;
+  if (t0 >= T) return;
+  float logit[kDotTok][kDotExp], amax[kDotTok];
+#pragma unroll
+  for (int u = 0; u < kDotTok; ++u) amax[u] = 0.0f;
+  v4f xv[kDotTok][kDotVec];
+  for (int base = 0; base < d; base += kDotPart) {
+    v4f wv[kDotExp][kDotVec];
+#pragma unroll
+    for (int j = 0; j < kDotVec; ++j) {
+      const int i = base + (j * 64 + lane) * 4;
+#pragma unroll
+      for (int u = 0; u < kDotTok; ++u)
+        xv[u][j] = (i < d && t0 + u < T) ? *reinterpret_cast<const v4f *>(x + (size_t)(t0 + u) * d + i)
+                                         : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < kDotExp; ++v)
+        wv[v][j] = (i < d && e0 + v < E) ? *reinterpret_cast<const v4f *>(wr + (size_t)(e0 + v) * d + i)
+                                         : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kDotTok; ++u) {
+#pragma unroll
+      for (int j = 0; j < kDotVec; ++j)
+        amax[u] = fmaxf(amax[u], fmaxf(fmaxf(fabsf(xv[u][j].x), fabsf(xv[u][j].y)),
+                                       fmaxf(fabsf(xv[u][j].z), fabsf(xv[u][j].w))));
+#pragma unroll
+      for (int v = 0; v < kDotExp; ++v) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kDotVec; ++j) {
+          acc = fmaf(xv[u][j].x, wv[v][j].x, acc);
+          acc = fmaf(xv[u][j].y, wv[v][j].y, acc);
+          acc = fmaf(xv[u][j].z, wv[v][j].z, acc);
+          acc = fmaf(xv[u][j].w, wv[v][j].w, acc);
+        }
+        const float ps = wave_sum(acc);
+        logit[u][v] = base == 0 ? ps : logit[u][v] + ps;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kDotTok; ++u) {
+    const int t = t0 + u;
+    if (t >= T) break;
+#pragma unroll
+    for (int v = 0; v < kDotExp; ++v) {
+      const int e = e0 + v;
+      if (e < E && lane == 0) logits[(size_t)t * E + e] = bias ? logit[u][v] + bias[e] : logit[u][v];
+    }
+    if (eq == 0 && xq) {
+      const float m = wave_max(amax[u]);
+      uint8_t *q = xq + (size_t)t * d;
+      if (d <= kDotPart) {
+        quantize_part_wave(xv[u], d, 0, m, q, lane);
+      } else {
+        const float r = m != 0.0f ? kE4m3Max / m : 1.0f;
+        const float *xr = x + (size_t)t * d;
+        for (int i = lane * 4; i < d; i += kWave * 4) {
+          const v4f v = *reinterpret_cast<const v4f *>(xr + i);
+          *reinterpret_cast<uint32_t *>(q + i) = e4m3x4(v.x * r, v.y * r, v.z * r, v.w * r);
+        }
+      }
+      if (lane == 0) sx[t] = m != 0.0f ? m / kE4m3Max : 1.0f;
+    }
+  }
+}
+
+// Small batches: one wave per (token, expert) product keeps more waves in flight.
 __global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict__ x,
                                                          const float *__restrict__ wr,
                                                          const float *__restrict__ bias, int T,
@@ -51,6 +139,20 @@ __global__ __launch_bounds__(256) void router_dot_kernel(const float *__restrict
   if (wid >= T * E) return;
   const int t = wid / E;
   router_dot_wave(x, wr, bias, d, E, logits, xq, sx, t, wid - t * E, threadIdx.x & 63);
+}
+
+static hipError_t launch_router_dot(const float *x, const float *w_router, const float *bias,
+                                    int32_t T, int32_t d, int32_t E, float *logits, uint8_t *xq,
+                                    float *sx, hipStream_t stream) {
+  if ((int64_t)T * E < kRouterDotTileMin) {
+    router_dot_kernel<<<(T * E + 3) / 4, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits, xq,
+                                                           sx);
+    return hipGetLastError();
+  }
+  const int64_t waves = (int64_t)((T + kDotTok - 1) / kDotTok) * ((E + kDotExp - 1) / kDotExp);
+  router_dot_tile_kernel<<<(int)((waves + 3) / 4), 256, 0, stream>>>(x, w_router, bias, T, d, E,
+                                                                     logits, xq, sx);
+  return hipGetLastError();
 }
 
 // Decode-sized batches: one workgroup per token computes its E logits (the
@@ -331,11 +433,8 @@ hipError_t launch_route_logits(const float *x, const float *w_router, const floa
                                int32_t d, int32_t E, float *logits, uint8_t *xq, float *sx,
                                hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if ((int64_t)T * E <= kRouterDotMax) {
-    router_dot_kernel<<<(T * E + 3) / 4, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits, xq,
-                                                           sx);
-    return hipGetLastError();
-  }
+  if ((int64_t)T * E <= kRouterDotMax)
+    return launch_router_dot(x, w_router, bias, T, d, E, logits, xq, sx, stream);
   hipError_t e = hipSuccess;
   if (xq && (e = launch_quantize_rows(x, T, d, xq, sx, stream)) != hipSuccess) return e;
   return launch_router(x, w_router, bias, T, d, E, logits, stream);
@@ -344,11 +443,8 @@ hipError_t launch_route_logits(const float *x, const float *w_router, const floa
 hipError_t launch_router(const float *x, const float *w_router, const float *bias, int32_t T,
                          int32_t d, int32_t E, float *logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if ((int64_t)T * E <= kRouterDotMax) {
-    router_dot_kernel<<<(T * E + 3) / 4, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits,
-                                                           nullptr, nullptr);
-    return hipGetLastError();
-  }
+  if ((int64_t)T * E <= kRouterDotMax)
+    return launch_router_dot(x, w_router, bias, T, d, E, logits, nullptr, nullptr, stream);
   if (route_tile_applies(T, E))  // the arithmetic of the fused prefill routing
     return launch_route_tile(x, w_router, bias, T, d, E, 0, nullptr, logits, nullptr, nullptr,
                              nullptr, nullptr, stream);

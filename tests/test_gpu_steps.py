@@ -76,6 +76,9 @@ def test_quantize_rows_bit_exact(rows, cols):
                                         # chunks, expert counts that pad the tile
                                         (1100, 64, 64, False), (3000, 192, 40, True),
                                         (3900, 128, 17, True), (2000, 320, 33, False),
+                                        # two tokens x four experts per wave: odd T, E not a
+                                        # multiple of 4, two 2048-float parts
+                                        (301, 256, 70, True), (200, 4096, 100, False),
                                         (1024, 2048, 512, True)])
 def test_router_logits(T, d, E, bias):
     g = torch.Generator().manual_seed(T + d + E)
@@ -103,12 +106,14 @@ def test_router_one_hot_exact(T, E):
 
 @pytest.mark.parametrize("T,d,E,k,var", [(1100, 256, 64, 6, False), (700, 320, 100, 8, True),
                                          (2100, 192, 32, 4, True), (4096, 2048, 128, 8, False),
-                                         (1100, 64, 64, 6, True), (3900, 128, 17, 17, False)])
+                                         (1100, 64, 64, 6, True), (3900, 128, 17, 17, False),
+                                         (301, 256, 70, 6, True), (200, 4096, 100, 8, False)])
 def test_prefill_routing_equals_steps(T, d, E, k, var):
-    """Past the per-(token, expert) kernels the layer routes in one launch
-    (logits, quantised x, top-k): its ids and weights equal, bit for bit, those
-    of moe_route_topk on moe_router_logits' logits, and the layer's output
-    matches the oracle run on those logits."""
+    """Whichever routing kernels the batch size picks (the one-launch prefill
+    routing here for T*E > 65536, two tokens x four experts per wave below it),
+    the layer's ids and weights equal, bit for bit, those of moe_route_topk on
+    moe_router_logits' logits, and the layer's output matches the oracle run
+    on those logits."""
     m = lib()
     spec = wl.TINY.with_(T=T, d=d, f=128, E=E, k=k, bias="zipf", bias_param=1.0,
                          k_choices=tuple(range(1, k + 1)) if var else ())
@@ -122,7 +127,7 @@ def test_prefill_routing_equals_steps(T, d, E, k, var):
     torch.cuda.synchronize()
     assert torch.equal(ids, ids_s)
     assert torch.equal(w, w_s)
-    rows = np.unique(np.random.default_rng(T).choice(T, 256, replace=False))
+    rows = np.unique(np.random.default_rng(T).choice(T, min(T, 256), replace=False))
     ref, _, _ = oracle.forward(to_np(L.x)[rows], L.qw, k, logits_override=to_np(lg)[rows],
                                k_per_token=None if kpt is None else to_np(kpt)[rows])
     err = rel_l2(to_np(out)[rows], ref)
