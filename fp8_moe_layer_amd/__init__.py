@@ -337,9 +337,9 @@ class MoELayer:
 
     forward(x) runs the whole layer (quantise, router, top-k, permutation,
     gate/up + SiLU*up, requantisation, down projection, combine) in the
-    library's kernels on the current stream -- seven launches, or one
-    cooperative launch with persistent=True.  The workspace is allocated once
-    per token count and reused.
+    library's kernels on the current stream -- six launches at decode sizes,
+    eight to ten at prefill sizes (persistent=True, one cooperative launch, is
+    refused).  The workspace is allocated once per token count and reused.
     """
 
     def __init__(self, weights: DeviceWeights, w_router: Optional[torch.Tensor], k_max: int,
