@@ -17,6 +17,9 @@ SPECS = {
     "tiny": wl.TINY,
     "zipf-two-shapes": wl.TINY.with_(T=64, d=512, f=256, E=128, k=8, bias="zipf", bias_param=2.0),
     "shared-elastic": wl.TINY.with_(T=48, d=256, f=192, E=16, k=4, n_shared=2, k_choices=(1, 2, 4)),
+    # routing by two tokens x four experts per wave, and in one prefill launch
+    "mid-routing": wl.TINY.with_(T=301, d=256, f=128, E=70, k=6, k_choices=(2, 4, 6)),
+    "prefill-routing": wl.TINY.with_(T=1100, d=256, f=128, E=64, k=6, n_shared=1),
 }
 
 
