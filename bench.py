@@ -52,7 +52,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--config", default="mixtral", choices=sorted(DEFAULT_T))
     p.add_argument("--tokens", type=int, default=0, help="batch size (default per config)")
     p.add_argument("--bias-param", type=float, default=None,
