@@ -233,15 +233,6 @@ hipError_t launch_route_topk_fused(const float *x, const float *w_router, const 
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void router_mfma_kernel(const float *__restrict__ x,
-                                                          const float *__restrict__ wr,
-                                                          const float *__restrict__ bias, int T,
-                                                          int d, int E, float *__restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) float lds[kRouterTileLdsFloats];
-  router_tile(x, wr, bias, T, d, E, logits, blockIdx.x * kRT, blockIdx.y * kRE, lds,
-              lds + kRT * kRS);
-}
-
 // ------------------------------------------------------------------ routing, prefill-sized
 // Batches with many tokens and at most 128 experts: one workgroup of eight
 // waves takes TT = 2048/EW tokens against all experts (EW: E padded to 32, 64
@@ -273,10 +264,12 @@ __global__ __launch_bounds__(kRtThreads) void route_tile_kernel(
   __shared__ float ls[TT * EW];
   __shared__ float ramax[TT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * TT;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * EW;  // experts [e0, e0 + EW) of this block
   const int tb = wave % TB, eb = wave / TB;
   const int lr = lane & 15, lq = lane >> 4;
   const int nch = d / kRtChunk;
+  // more than one expert block (E > EW): only block 0 quantises, top-k is left to the caller
+  if (blockIdx.y != 0) xq = nullptr;
 
   // Each thread's staging slots: a fixed source row (clamped into range, so
   // every load is issued unconditionally and the wait counts stay exact) and
@@ -291,7 +284,7 @@ __global__ __launch_bounds__(kRtThreads) void route_tile_kernel(
       real[j] = i < NV && t < T;
       src[j] = x + (size_t)(t < T ? t : T - 1) * d + c;
     } else {
-      const int e = r - TT;
+      const int e = e0 + r - TT;
       real[j] = i < NV && e < E;
       src[j] = wr + (size_t)(e < E ? e : E - 1) * d + c;
     }
@@ -354,16 +347,16 @@ __global__ __launch_bounds__(kRtThreads) void route_tile_kernel(
   }
 
   // logits: tile rows are tokens, columns experts
-  const int e = eb * 16 + lr;
+  const int el = eb * 16 + lr, e = e0 + el;
   const float be = (bias && e < E) ? bias[e] : 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = tb * 16 + 4 * lq + i, t = t0 + r;
     const float lg = bias ? acc[i] + be : acc[i];
-    ls[r * EW + e] = lg;
+    ls[r * EW + el] = lg;
     if (t < T && e < E) logits[(size_t)t * E + e] = lg;
   }
-  if (!xq) return;
+  if (!xq) return;  // logits only, or an expert block past the first
   // each token row's |x| maximum: the 16 lanes that loaded it are one DPP row
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
@@ -398,8 +391,9 @@ __global__ __launch_bounds__(kRtThreads) void route_tile_kernel(
       }
     }
     if (lane == 0) sx[t] = m != 0.0f ? m / kE4m3Max : 1.0f;
-    topk_row_wave(ls + r * EW, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
-                  w + (size_t)t * k_max, lane);
+    if (ids)  // all experts in this block (E <= EW)
+      topk_row_wave(ls + r * EW, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+                    w + (size_t)t * k_max, lane);
   }
 }
 
@@ -416,8 +410,9 @@ static hipError_t launch_route_tile(const float *x, const float *w_router, const
     route_tile_kernel<32><<<(T + 63) / 64, kRtThreads, 0, stream>>>(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w);
   else if (E <= 64)
     route_tile_kernel<64><<<(T + 31) / 32, kRtThreads, 0, stream>>>(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w);
-  else
-    route_tile_kernel<128><<<(T + 15) / 16, kRtThreads, 0, stream>>>(x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, ids, w);
+  else  // E > 128: blocks of 128 experts along y; the caller runs the top-k
+    route_tile_kernel<128><<<dim3((T + 15) / 16, (E + 127) / 128), kRtThreads, 0, stream>>>(
+        x, w_router, bias, T, d, E, k_max, kpt, logits, xq, sx, E <= 128 ? ids : nullptr, w);
   return hipGetLastError();
 }
 
@@ -435,6 +430,9 @@ hipError_t launch_route_logits(const float *x, const float *w_router, const floa
   if (T == 0) return hipSuccess;
   if ((int64_t)T * E <= kRouterDotMax)
     return launch_router_dot(x, w_router, bias, T, d, E, logits, xq, sx, stream);
+  if (E > 128)  // the tiled router over expert blocks, quantising x in its first block
+    return launch_route_tile(x, w_router, bias, T, d, E, 0, nullptr, logits, xq, sx, nullptr,
+                             nullptr, stream);
   hipError_t e = hipSuccess;
   if (xq && (e = launch_quantize_rows(x, T, d, xq, sx, stream)) != hipSuccess) return e;
   return launch_router(x, w_router, bias, T, d, E, logits, stream);
@@ -445,12 +443,9 @@ hipError_t launch_router(const float *x, const float *w_router, const float *bia
   if (T == 0) return hipSuccess;
   if ((int64_t)T * E <= kRouterDotMax)
     return launch_router_dot(x, w_router, bias, T, d, E, logits, nullptr, nullptr, stream);
-  if (route_tile_applies(T, E))  // the arithmetic of the fused prefill routing
-    return launch_route_tile(x, w_router, bias, T, d, E, 0, nullptr, logits, nullptr, nullptr,
-                             nullptr, nullptr, stream);
-  dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
-  router_mfma_kernel<<<grid, 256, 0, stream>>>(x, w_router, bias, T, d, E, logits);
-  return hipGetLastError();
+  // the arithmetic of the fused routing (one expert block, or blocks of 128)
+  return launch_route_tile(x, w_router, bias, T, d, E, 0, nullptr, logits, nullptr, nullptr,
+                           nullptr, nullptr, stream);
 }
 
 // ------------------------------------------------------------------ top-k

@@ -79,7 +79,8 @@ def test_quantize_rows_bit_exact(rows, cols):
                                         # two tokens x four experts per wave: odd T, E not a
                                         # multiple of 4, two 2048-float parts
                                         (301, 256, 70, True), (200, 4096, 100, False),
-                                        (1024, 2048, 512, True)])
+                                        # blocks of 128 experts (the last one ragged)
+                                        (700, 256, 300, True), (1024, 2048, 512, True)])
 def test_router_logits(T, d, E, bias):
     g = torch.Generator().manual_seed(T + d + E)
     x = torch.randn(T, d, generator=g)
@@ -107,10 +108,13 @@ def test_router_one_hot_exact(T, E):
 @pytest.mark.parametrize("T,d,E,k,var", [(1100, 256, 64, 6, False), (700, 320, 100, 8, True),
                                          (2100, 192, 32, 4, True), (4096, 2048, 128, 8, False),
                                          (1100, 64, 64, 6, True), (3900, 128, 17, 17, False),
-                                         (301, 256, 70, 6, True), (200, 4096, 100, 8, False)])
+                                         (301, 256, 70, 6, True), (200, 4096, 100, 8, False),
+                                         (700, 256, 300, 16, True)])
 def test_prefill_routing_equals_steps(T, d, E, k, var):
     """Whichever routing kernels the batch size picks (the one-launch prefill
-    routing here for T*E > 65536, two tokens x four experts per wave below it),
+    routing for T*E > 65536 and E <= 128, the same tile over blocks of 128
+    experts then a top-k launch for E > 128, two tokens x four experts per wave
+    below 65536 pairs),
     the layer's ids and weights equal, bit for bit, those of moe_route_topk on
     moe_router_logits' logits, and the layer's output matches the oracle run
     on those logits."""
