@@ -153,7 +153,9 @@ def _tie_logits(T, E, seed):
 
 @pytest.mark.parametrize("T,E,k,var", [(16, 8, 2, False), (64, 128, 8, False), (31, 64, 6, False),
                                        (100, 512, 32, True), (7, 5, 5, False), (40, 32, 1, False),
-                                       (1024, 512, 32, True)])
+                                       (1024, 512, 32, True),
+                                       # just past one and two 64-expert slots per lane
+                                       (33, 65, 7, False), (50, 200, 32, True)])
 def test_topk_bit_exact(T, E, k, var):
     l = _tie_logits(T, E, T + E)
     kpt = None
