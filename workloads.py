@@ -15,7 +15,9 @@ W_r ~ N(0, 1/d); W_gate, W_up ~ N(0, 1/d); W_down ~ N(0, 1/f); all fp32.
 """
 from __future__ import annotations
 
+import json
 import math
+import os
 import zlib
 from dataclasses import dataclass, field, replace
 from typing import Optional
@@ -52,7 +54,37 @@ SPECS = {s.name: s for s in (TINY, MIXTRAL, QWEN3, DEEPSEEK, PRISM)}
 
 MIXTRAL_DECODE_T = (1, 8, 32, 128, 256)
 QWEN3_T = (64, 4096)
+QWEN3_D_TARGETS = (16, 32, 64, 96)  # distinct active experts at T=64 (alpha = 0 gives ~126)
 DEEPSEEK_T = (32, 512, 8192)
+
+# Router biases calibrated on the CPU oracle's routing (tests/golden/
+# make_routing_bias.py writes this file): the DeepSeek-shaped hot expert's
+# logit bias per batch size (the hot expert then receives 4x the mean load),
+# and the Qwen3-shaped Zipf alpha per target number of distinct experts.
+ROUTING_BIAS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden",
+                                 "routing_bias.json")
+
+
+def _routing_bias() -> dict:
+    with open(ROUTING_BIAS_FILE) as fh:
+        return json.load(fh)
+
+
+def deepseek_spec(T: int) -> "LayerSpec":
+    """The DeepSeek-shaped layer at batch T (first T rows of the 8192-token
+    draw) with the hot-expert bias calibrated for T."""
+    ent = _routing_bias()["deepseek_hot"][str(T)]
+    return DEEPSEEK.with_(T=T, bias="hot", bias_param=float(ent["beta"]))
+
+
+def deepseek_hot_target(T: int) -> int:
+    """Tokens the hot expert receives at batch T: 4x the mean load."""
+    return int(round(4 * T * DEEPSEEK.k / DEEPSEEK.E))
+
+
+def qwen3_alpha(D: int) -> float:
+    """Zipf alpha that makes the T=64 Qwen3-shaped batch activate D experts."""
+    return float(_routing_bias()["qwen3_zipf"][str(D)]["alpha"])
 
 
 def _seed(seed: int, name: str, idx: int = 0) -> int:
@@ -87,13 +119,7 @@ def routing_inputs(spec: LayerSpec, seed: int = 0) -> RoutingInputs:
     wr = normal((spec.E, spec.d), 1.0 / math.sqrt(spec.d), seed, "w_router")
     bias = None
     if spec.bias == "zipf" and spec.bias_param != 0.0:
-        # b_e = alpha * ln p_{pi(e)}, p_r proportional to r^-s, pi a seeded
-        # permutation so the hot experts are not simply the low indices.
-        perm = torch.randperm(spec.E, generator=_gen(seed, "zipf_perm"))
-        ranks = torch.arange(1, spec.E + 1, dtype=torch.float64)
-        p = ranks.pow(-spec.zipf_s)
-        p = p / p.sum()
-        bias = (spec.bias_param * torch.log(p))[perm].to(torch.float32).contiguous()
+        bias = zipf_bias(spec, seed)
     elif spec.bias == "hot" and spec.bias_param != 0.0:
         hot = int(torch.randint(spec.E, (1,), generator=_gen(seed, "hot_expert")).item())
         bias = torch.zeros(spec.E, dtype=torch.float32)
@@ -107,6 +133,19 @@ def routing_inputs(spec: LayerSpec, seed: int = 0) -> RoutingInputs:
         sel = torch.randint(len(spec.k_choices), (spec.T,), generator=_gen(seed, "k_per_token"))
         kpt = ch[sel].contiguous()
     return RoutingInputs(x, wr, bias, kpt)
+
+
+def zipf_bias(spec: LayerSpec, seed: int = 0) -> Optional[torch.Tensor]:
+    """b_e = alpha * ln p_{pi(e)} with p_r proportional to r^-s (s = 1.1) and
+    pi a seeded permutation, so the hot experts are not simply the low
+    indices; None for alpha = 0."""
+    if spec.bias_param == 0.0:
+        return None
+    perm = torch.randperm(spec.E, generator=_gen(seed, "zipf_perm"))
+    ranks = torch.arange(1, spec.E + 1, dtype=torch.float64)
+    p = ranks.pow(-spec.zipf_s)
+    p = p / p.sum()
+    return (spec.bias_param * torch.log(p))[perm].to(torch.float32).contiguous()
 
 
 def hot_expert_index(spec: LayerSpec, seed: int = 0) -> int:
