@@ -20,6 +20,7 @@ LIB_PATH = _HERE / "libfp8moe.so"
 
 MOE_F_NO_REQUANT = 1
 MOE_F_PERSISTENT = 2
+MOE_F_FUSED_COMBINE = 4
 MAX_EXPERTS = 512
 MAX_K = 32
 
@@ -69,7 +70,8 @@ _fused_forward = _sig("moe_fused_forward", _i32, _DP, _vp, _vp, _vp, _vp, _WP, _
 _status_str = _sig("moe_status_str", C.c_char_p, _i32)
 _last_error = _sig("moe_last_error", C.c_char_p)
 _abi_version = _sig("moe_abi_version", _i32)
-_debug_stage_events = _sig("moe_debug_stage_events", _i32, C.POINTER(_vp), _i32)
+_fused_forward_timed = _sig("moe_fused_forward_timed", _i32, _DP, _vp, _vp, _vp, _vp, _WP, _vp,
+                            _vp, _vp, _vp, _vp, C.c_size_t, C.POINTER(_vp), _i32, _vp)
 _group_tokens = _sig("moe_group_tokens", _i32, _vp, _i32, _i32, _i32, _i32, _vp)
 _k_tiers = _sig("moe_k_tiers", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 
@@ -108,15 +110,12 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
-def set_stage_events(handles):
-    """Make moe_fused_forward (on this thread) record the given hipEvent_t
-    handles around its stages (instrumentation); None stops it."""
-    if handles is None:
-        _check(_debug_stage_events(None, 0))
-        return None
-    arr = (_vp * len(handles))(*handles)
-    _check(_debug_stage_events(arr, len(handles)))
-    return arr  # the caller keeps this alive while the events are in use
+def _on(stream):
+    """Context in which new tensors are allocated for `stream` (the caching
+    allocator then never hands their memory to another stream while work on
+    this one may still use it)."""
+    import contextlib
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 # --------------------------------------------------------------------------- steps
@@ -359,27 +358,38 @@ class MoELayer:
         return dims(T, self.w.d, self.w.f, self.w.E, self.k_max, self.w.n_shared, self.block_m,
                     self.no_requant, self.persistent)
 
-    def workspace(self, T: int, device) -> torch.Tensor:
-        ws = self._ws.get(T)
+    def workspace(self, T: int, device, stream=None) -> torch.Tensor:
+        """The workspace for T tokens, allocated on `stream` (the stream the
+        layer's kernels will use) and kept until T changes."""
+        key = (T, None if stream is None else stream.cuda_stream)
+        ws = self._ws.get(key)
         if ws is None:
             n = workspace_bytes(self.dims(T))
             if n == 0:
                 raise MoEError(int(2))
-            ws = torch.empty(n, dtype=torch.uint8, device=device)
-            self._ws = {T: ws}
+            with _on(stream):
+                ws = torch.empty(n, dtype=torch.uint8, device=device)
+            self._ws = {key: ws}
         return ws
 
     def forward(self, x: torch.Tensor, k_per_token=None, logits_override=None, out=None,
-                topk_ids=None, topk_w=None, stream=None) -> torch.Tensor:
+                topk_ids=None, topk_w=None, stream=None, stage_events=None) -> torch.Tensor:
+        """stream: a torch.cuda.Stream (default: the current one); stage_events:
+        MOE_N_STAGE_EVENTS hipEvent_t handles recorded around the stages
+        (instrumentation), or None."""
         T = x.shape[0]
         dm = self.dims(T)
-        out = torch.empty((T, self.w.d), dtype=torch.float32, device=x.device) if out is None else out
-        ws = self.workspace(T, x.device)
-        _check(_fused_forward(C.byref(dm), _ptr(x, torch.float32), _ptr(self.w_router, torch.float32),
-                              _ptr(self.router_bias, torch.float32), _ptr(k_per_token, torch.int32),
-                              C.byref(self._wstruct), _ptr(logits_override, torch.float32), _ptr(out),
-                              _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), _ptr(ws),
-                              ws.numel(), _stream(stream)))
+        if out is None:
+            with _on(stream):
+                out = torch.empty((T, self.w.d), dtype=torch.float32, device=x.device)
+        ws = self.workspace(T, x.device, stream)
+        ev = None if stage_events is None else (_vp * len(stage_events))(*stage_events)
+        _check(_fused_forward_timed(
+            C.byref(dm), _ptr(x, torch.float32), _ptr(self.w_router, torch.float32),
+            _ptr(self.router_bias, torch.float32), _ptr(k_per_token, torch.int32),
+            C.byref(self._wstruct), _ptr(logits_override, torch.float32), _ptr(out),
+            _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), _ptr(ws), ws.numel(), ev,
+            0 if ev is None else len(stage_events), _stream(stream)))
         return out
 
     __call__ = forward

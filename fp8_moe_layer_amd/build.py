@@ -31,21 +31,42 @@ def _hipcc() -> str:
     return str(cand) if cand.exists() else "hipcc"
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> pathlib.Path:
-    """Compile every HIP source into libfp8moe.so (always recompiles)."""
-    tmp = LIB.with_name(LIB.name + ".tmp")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-o", str(tmp)] + [str(CSRC / s) for s in SOURCES]
-    if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and (verbose or resource_usage):
-        print(err, file=sys.stderr)
+    return res.returncode, err
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> pathlib.Path:
+    """Compile every HIP source into libfp8moe.so (always recompiles; the
+    sources compile in parallel, then link)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = HERE / "_build"
+    objdir.mkdir(exist_ok=True)
+    tmp = LIB.with_name(LIB.name + ".tmp")
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    if resource_usage:
+        flags = ["-Rpass-analysis=kernel-resource-usage"] + flags
+    jobs = []
+    for s in SOURCES:
+        obj = objdir / (pathlib.Path(s).stem + ".o")
+        jobs.append((obj, [_hipcc(), *flags, "-c", "-o", str(obj), str(CSRC / s)]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(workers) as pool:
+        results = list(pool.map(lambda j: _run(j[1], verbose), jobs))
+    for (obj, _), (rc, err) in zip(jobs, results):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {obj.stem} ({rc}):\n{err}")
+        if err.strip() and (verbose or resource_usage):
+            print(err, file=sys.stderr)
+    rc, err = _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp)] +
+                   [str(o) for o, _ in jobs], verbose)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     tmp.replace(LIB)
     return LIB
 

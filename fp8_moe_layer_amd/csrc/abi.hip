@@ -1,7 +1,7 @@
 // abi.hip -- the C ABI (include/fp8moe.h): host-side validation, workspace
 // layout, tile-shape choice and kernel enqueueing.  No allocation, no
 // synchronisation, no state kept between calls except the thread-local error
-// text.
+// text and each device's compute-unit count.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/fp8moe.h"
 #include "internal.hpp"
@@ -18,7 +20,6 @@ using namespace fp8moe;
 namespace {
 
 thread_local char g_err[512] = "";
-thread_local hipEvent_t const *g_stage_events = nullptr;
 
 moe_status fail(moe_status code, const char *fmt, ...) {
   va_list ap;
@@ -75,6 +76,10 @@ moe_status check_dims(const moe_dims *d, const char *fn) {
   if (d->n_shared < 0) return fail(MOE_ERR_SHAPE, "%s: n_shared=%d must be >= 0", fn, d->n_shared);
   if (!block_m_ok(d->block_m))
     return fail(MOE_ERR_SHAPE, "%s: block_m=%d must be 1, 16, 32, 64 or 128", fn, d->block_m);
+  if (d->flags & MOE_F_FUSED_COMBINE)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: MOE_F_FUSED_COMBINE is not built (the combine runs in slot order in its own "
+                "kernel)", fn);
   if (d->flags & ~(uint32_t)(MOE_F_NO_REQUANT | MOE_F_PERSISTENT))
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown flags 0x%x", fn, d->flags);
   // all row indices must fit in int32
@@ -191,9 +196,28 @@ struct GemmPlan {
   int32_t waves, splits, nb;
 };
 
-constexpr int kCUs = 256;
+// Compute units of the current device, queried once per device ordinal
+// (256 on MI355X; the planner's rounds depend on it).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
+  const int kCUs = device_cus();
   const double items = expected_items(d, msub);
   const int N = gate_up ? d->f : d->d;
   const int K = gate_up ? d->d : d->f;
@@ -301,6 +325,133 @@ Layout layout_of(const moe_dims *d) {
   return L;
 }
 
+RowSpace row_space(const moe_dims *d, int32_t capacity, const int32_t *sorted_pairs,
+                          const int32_t *expert_offsets) {
+  RowSpace rs{};
+  rs.T = d->T;
+  rs.d = d->d;
+  rs.f = d->f;
+  rs.E = d->E;
+  rs.S = d->n_shared;
+  rs.k_max = d->k_max;
+  rs.capacity = capacity;
+  rs.sorted_pairs = sorted_pairs;
+  rs.expert_offsets = expert_offsets;
+  return rs;
+}
+
+// Host-side checks of moe_fused_forward's arguments (everything but the
+// workspace).
+moe_status check_forward(const moe_dims *dims, const float *x, const float *w_router,
+                         const moe_weights *w, const float *logits_override, const float *out,
+                         const char *fn) {
+  moe_status s = check_dims(dims, fn);
+  if (s) return s;
+  // The single-launch path (kernels_persistent.hip) is switched off: under
+  // test on gfx950 its cooperative launch did not complete (the grid-wide
+  // barrier never released) and the cause is not established.
+  if (dims->flags & MOE_F_PERSISTENT)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: MOE_F_PERSISTENT is switched off in this build", fn);
+  if ((s = check_weights(dims, w, fn))) return s;
+  if (!x || !out) return fail(MOE_ERR_NULL, "%s: x and out are required", fn);
+  if (!w_router && !logits_override)
+    return fail(MOE_ERR_NULL, "%s: w_router is required unless logits_override is given", fn);
+  if (!aligned(x, 16) || !aligned(out, 16) || (w_router && !aligned(w_router, 16)))
+    return fail(MOE_ERR_ALIGN, "%s: x, out and w_router must be 16-byte aligned", fn);
+  return MOE_OK;
+}
+
+// Enqueues the whole layer on `st` with workspace `ws` laid out as L;
+// ev: NULL, or MOE_N_STAGE_EVENTS events recorded around the stages.
+moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_router,
+                           const float *router_bias, const int32_t *k_per_token,
+                           const moe_weights *w, const float *logits_override, float *out,
+                           int32_t *topk_ids_out, float *topk_w_out, char *ws, const Layout &L,
+                           hipEvent_t const *ev, hipStream_t st) {
+  moe_status s = MOE_OK;
+  uint8_t *xq = reinterpret_cast<uint8_t *>(ws + L.xq);
+  float *sx = reinterpret_cast<float *>(ws + L.sx);
+  float *logits = reinterpret_cast<float *>(ws + L.logits);
+  int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(ws + L.ids);
+  float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(ws + L.w);
+  int32_t *sorted = reinterpret_cast<int32_t *>(ws + L.sorted);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  int32_t *block_expert = reinterpret_cast<int32_t *>(ws + L.block_expert);
+  int32_t *inv = reinterpret_cast<int32_t *>(ws + L.inv);
+  int32_t *n_blocks = reinterpret_cast<int32_t *>(ws + L.n_blocks);
+  WorkItem *items = reinterpret_cast<WorkItem *>(ws + L.items);
+  int32_t *n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
+  float *h = reinterpret_cast<float *>(ws + L.h);
+  uint8_t *hq = reinterpret_cast<uint8_t *>(ws + L.hq);
+  float *sh = reinterpret_cast<float *>(ws + L.sh);
+  float *y = reinterpret_cast<float *>(ws + L.y);
+  const bool requant = !(dims->flags & MOE_F_NO_REQUANT);
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], st);
+  };
+
+  mark(0);
+  const float *lg = logits_override;
+  if (!lg && route_fused_applies(dims->T, dims->E)) {
+    // one launch: logits, quantised x, top-k
+    if ((s = hip_status(launch_route_topk_fused(x, w_router, router_bias, dims->T, dims->d,
+                                                dims->E, dims->k_max, k_per_token, logits, xq, sx,
+                                                ids, tw, st),
+                        "route")))
+      return s;
+    mark(1);
+  } else if (!lg && route_tile_applies(dims->T, dims->E)) {
+    if ((s = hip_status(launch_route_prefill(x, w_router, router_bias, dims->T, dims->d, dims->E,
+                                             dims->k_max, k_per_token, logits, xq, sx, ids, tw, st),
+                        "route")))
+      return s;
+    mark(1);
+  } else {
+    if (!lg) {
+      if ((s = hip_status(launch_route_logits(x, w_router, router_bias, dims->T, dims->d, dims->E,
+                                              logits, xq, sx, st),
+                          "router")))
+        return s;
+      lg = logits;
+    } else if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) {
+      return s;
+    }
+    mark(1);
+    if ((s = hip_status(launch_topk(lg, dims->T, dims->E, dims->k_max, k_per_token, ids, tw, st),
+                        "topk")))
+      return s;
+  }
+  mark(2);
+  if ((s = hip_status(launch_permute(ids, dims->T, dims->E, dims->k_max, dims->block_m, L.capacity,
+                                     sorted, offsets, block_expert, inv, n_blocks, items, n_items,
+                                     L.row_chunk, dims->n_shared, st),
+                      "permute")))
+    return s;
+  RowSpace rs = row_space(dims, L.capacity, sorted, offsets);
+  rs.items = items;
+  rs.n_items = n_items;
+  rs.max_items = L.max_items;
+  const ExpertWeights ew = to_internal(w);
+  mark(3);
+  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, L.nt_gu, st), "gate_up"))) return s;
+  mark(4);
+  if (requant) {
+    if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
+    mark(5);
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
+                        "down")))
+      return s;
+  } else {
+    mark(5);
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, false, st), "down")))
+      return s;
+  }
+  mark(6);
+  if ((s = hip_status(launch_combine(rs, y, L.splits, ids, tw, inv, out, st), "combine"))) return s;
+  mark(7);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,18 +472,6 @@ const char *moe_status_str(moe_status s) {
 const char *moe_last_error(void) { return g_err; }
 
 int32_t moe_abi_version(void) { return FP8MOE_ABI_VERSION; }
-
-moe_status moe_debug_stage_events(void *const *events, int32_t n_events) {
-  if (!events || n_events == 0) {
-    g_stage_events = nullptr;
-    return ok();
-  }
-  if (n_events < MOE_N_STAGE_EVENTS)
-    return fail(MOE_ERR_SHAPE, "moe_debug_stage_events: %d events given, %d needed", n_events,
-                MOE_N_STAGE_EVENTS);
-  g_stage_events = reinterpret_cast<hipEvent_t const *>(events);
-  return ok();
-}
 
 int64_t moe_capacity(int32_t T, int32_t E, int32_t k_max, int32_t block_m) {
   return capacity_of(T, E, k_max, block_m);
@@ -418,20 +557,6 @@ moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_
   return s ? s : ok();
 }
 
-static RowSpace row_space(const moe_dims *d, int32_t capacity, const int32_t *sorted_pairs,
-                          const int32_t *expert_offsets) {
-  RowSpace rs{};
-  rs.T = d->T;
-  rs.d = d->d;
-  rs.f = d->f;
-  rs.E = d->E;
-  rs.S = d->n_shared;
-  rs.k_max = d->k_max;
-  rs.capacity = capacity;
-  rs.sorted_pairs = sorted_pairs;
-  rs.expert_offsets = expert_offsets;
-  return rs;
-}
 
 static moe_status check_stage(const moe_dims *dims, int32_t capacity, const moe_weights *w,
                               const int32_t *sorted_pairs, const int32_t *expert_offsets,
@@ -520,111 +645,32 @@ moe_status moe_fused_forward(const moe_dims *dims, const float *x, const float *
                              const moe_weights *w, const float *logits_override, float *out,
                              int32_t *topk_ids_out, float *topk_w_out, void *workspace,
                              size_t workspace_bytes, void *stream) {
+  return moe_fused_forward_timed(dims, x, w_router, router_bias, k_per_token, w, logits_override,
+                                 out, topk_ids_out, topk_w_out, workspace, workspace_bytes, nullptr,
+                                 0, stream);
+}
+
+moe_status moe_fused_forward_timed(const moe_dims *dims, const float *x, const float *w_router,
+                                   const float *router_bias, const int32_t *k_per_token,
+                                   const moe_weights *w, const float *logits_override, float *out,
+                                   int32_t *topk_ids_out, float *topk_w_out, void *workspace,
+                                   size_t workspace_bytes, void *const *stage_events,
+                                   int32_t n_events, void *stream) {
   const char *fn = "moe_fused_forward";
-  moe_status s = check_dims(dims, fn);
+  moe_status s = check_forward(dims, x, w_router, w, logits_override, out, fn);
   if (s) return s;
-  // The single-launch path (kernels_persistent.hip) is switched off: under
-  // test on gfx950 its cooperative launch did not complete (the grid-wide
-  // barrier never released) and the cause is not established.
-  if (dims->flags & MOE_F_PERSISTENT)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: MOE_F_PERSISTENT is switched off in this build", fn);
-  if ((s = check_weights(dims, w, fn))) return s;
-  if (!x || !out) return fail(MOE_ERR_NULL, "%s: x and out are required", fn);
-  if (!w_router && !logits_override)
-    return fail(MOE_ERR_NULL, "%s: w_router is required unless logits_override is given", fn);
-  if (!aligned(x, 16) || !aligned(out, 16) || (w_router && !aligned(w_router, 16)))
-    return fail(MOE_ERR_ALIGN, "%s: x, out and w_router must be 16-byte aligned", fn);
+  if (stage_events && n_events < MOE_N_STAGE_EVENTS)
+    return fail(MOE_ERR_SHAPE, "%s: %d stage events given, %d needed", fn, n_events,
+                MOE_N_STAGE_EVENTS);
   const Layout L = layout_of(dims);
   if (!workspace || workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
                 workspace ? workspace_bytes : (size_t)0, L.total);
   if (!aligned(workspace, 256))
     return fail(MOE_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-
-  hipStream_t st = as_stream(stream);
-  char *ws = static_cast<char *>(workspace);
-  uint8_t *xq = reinterpret_cast<uint8_t *>(ws + L.xq);
-  float *sx = reinterpret_cast<float *>(ws + L.sx);
-  float *logits = reinterpret_cast<float *>(ws + L.logits);
-  int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(ws + L.ids);
-  float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(ws + L.w);
-  int32_t *sorted = reinterpret_cast<int32_t *>(ws + L.sorted);
-  int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
-  int32_t *block_expert = reinterpret_cast<int32_t *>(ws + L.block_expert);
-  int32_t *inv = reinterpret_cast<int32_t *>(ws + L.inv);
-  int32_t *n_blocks = reinterpret_cast<int32_t *>(ws + L.n_blocks);
-  WorkItem *items = reinterpret_cast<WorkItem *>(ws + L.items);
-  int32_t *n_items = reinterpret_cast<int32_t *>(ws + L.n_items);
-  float *h = reinterpret_cast<float *>(ws + L.h);
-  uint8_t *hq = reinterpret_cast<uint8_t *>(ws + L.hq);
-  float *sh = reinterpret_cast<float *>(ws + L.sh);
-  float *y = reinterpret_cast<float *>(ws + L.y);
-  const bool requant = !(dims->flags & MOE_F_NO_REQUANT);
-  hipEvent_t const *ev = g_stage_events;
-  auto mark = [&](int i) {
-    if (ev) (void)hipEventRecord(ev[i], st);
-  };
-
-  mark(0);
-  const float *lg = logits_override;
-  if (!lg && route_fused_applies(dims->T, dims->E)) {
-    // one launch: logits, quantised x, top-k
-    if ((s = hip_status(launch_route_topk_fused(x, w_router, router_bias, dims->T, dims->d,
-                                                dims->E, dims->k_max, k_per_token, logits, xq, sx,
-                                                ids, tw, st),
-                        "route")))
-      return s;
-    mark(1);
-  } else if (!lg && route_tile_applies(dims->T, dims->E)) {
-    if ((s = hip_status(launch_route_prefill(x, w_router, router_bias, dims->T, dims->d, dims->E,
-                                             dims->k_max, k_per_token, logits, xq, sx, ids, tw, st),
-                        "route")))
-      return s;
-    mark(1);
-  } else {
-    if (!lg) {
-      if ((s = hip_status(launch_route_logits(x, w_router, router_bias, dims->T, dims->d, dims->E,
-                                              logits, xq, sx, st),
-                          "router")))
-        return s;
-      lg = logits;
-    } else if ((s = hip_status(launch_quantize_rows(x, dims->T, dims->d, xq, sx, st), "quantize"))) {
-      return s;
-    }
-    mark(1);
-    if ((s = hip_status(launch_topk(lg, dims->T, dims->E, dims->k_max, k_per_token, ids, tw, st),
-                        "topk")))
-      return s;
-  }
-  mark(2);
-  if ((s = hip_status(launch_permute(ids, dims->T, dims->E, dims->k_max, dims->block_m, L.capacity,
-                                     sorted, offsets, block_expert, inv, n_blocks, items, n_items,
-                                     L.row_chunk, dims->n_shared, st),
-                      "permute")))
-    return s;
-  RowSpace rs = row_space(dims, L.capacity, sorted, offsets);
-  rs.items = items;
-  rs.n_items = n_items;
-  rs.max_items = L.max_items;
-  const ExpertWeights ew = to_internal(w);
-  mark(3);
-  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, L.nt_gu, st), "gate_up"))) return s;
-  mark(4);
-  if (requant) {
-    if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
-    mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
-                        "down")))
-      return s;
-  } else {
-    mark(5);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, false, st), "down")))
-      return s;
-  }
-  mark(6);
-  if ((s = hip_status(launch_combine(rs, y, L.splits, ids, tw, inv, out, st), "combine"))) return s;
-  mark(7);
-  return ok();
+  return enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
+                         topk_ids_out, topk_w_out, static_cast<char *>(workspace), L,
+                         reinterpret_cast<hipEvent_t const *>(stage_events), as_stream(stream));
 }
 
 }  // extern "C"

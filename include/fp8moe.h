@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FP8MOE_ABI_VERSION 3
+#define FP8MOE_ABI_VERSION 4
 
 typedef int32_t moe_status;
 enum {
@@ -69,11 +69,18 @@ enum {
 enum {
   MOE_F_NO_REQUANT = 1u << 0, /* keep SiLU*up in fp32 and run the down projection on fp32
                                  products; an accuracy mode, not a fast path */
-  MOE_F_PERSISTENT = 1u << 1  /* reserved for running moe_fused_forward as one cooperative
+  MOE_F_PERSISTENT = 1u << 1, /* reserved for running moe_fused_forward as one cooperative
                                  launch (the fused single kernel of the Alpha-MoE article,
                                  section "Comment fonctionne le megakernel").  Switched off in
                                  this build: moe_fused_forward returns MOE_ERR_UNSUPPORTED
                                  when it is set */
+  MOE_F_FUSED_COMBINE = 1u << 2 /* reserved for a combine fused into the down projection's
+                                 epilogue.  Not built: with expert-major tiles the only fusion
+                                 is a floating-point accumulation of each token's slots in
+                                 arrival order, which is neither in slot order nor
+                                 reproducible run to run; the weighted sum here is taken in
+                                 slot order by its own kernel.  Every call that takes dims
+                                 returns MOE_ERR_UNSUPPORTED when it is set */
 };
 
 /* Limits checked by every call. */
@@ -95,6 +102,12 @@ typedef struct {
 
 /* Expert weights: e4m3 codes (one byte each) in MFMA tile order, and fp32
  * per-output-channel scales.
+ *
+ * The tile order is part of the boundary on purpose: the grouped GEMMs
+ * stream every active expert's weights from HBM once per step, and in this
+ * order each 16-byte load of a wave belongs to a fully contiguous 1 KB piece
+ * (row-major rows would need 16 separate 64-byte half-lines per load).
+ * moe_pack_weights converts row-major codes once, at weight-load time.
  *
  * Tile order of a code matrix W [R][C] (R output channels, a multiple of 16;
  * C inputs, a multiple of 64), as written by moe_pack_weights: with
@@ -275,16 +288,23 @@ moe_status moe_k_tiers(const int32_t *k_per_token /*host*/, int32_t n, int32_t b
 
 /* ------------------------------------------------------------------------ */
 
-/* Stage timing (instrumentation, not part of the layer).  After this call,
- * moe_fused_forward on the calling thread records events[i] on its stream
- * just before stage i (0 quantise + router logits, 1 top-k, 2 permutation,
- * 3 gate/up, 4 requantisation, 5 down, 6 combine) and events[7] after the
- * last one.  `events` is a host array of MOE_N_STAGE_EVENTS hipEvent_t
- * handles created and owned by the caller; the library keeps the pointer
- * until the next call.  Pass NULL, 0 to stop.  Returns MOE_ERR_SHAPE when
- * 0 < n_events < MOE_N_STAGE_EVENTS. */
+/* Stage timing (instrumentation, not part of the layer): moe_fused_forward
+ * that also records stage_events[i] on its stream just before stage i
+ * (0 quantise + router logits, 1 top-k, 2 permutation, 3 gate/up,
+ * 4 requantisation, 5 down, 6 combine) and stage_events[7] after the last
+ * one.  stage_events: host array of n_events >= MOE_N_STAGE_EVENTS hipEvent_t
+ * handles created and owned by the caller, or NULL (then identical to
+ * moe_fused_forward).  The library records the events during this call only
+ * and keeps nothing.  Returns MOE_ERR_SHAPE when stage_events is given with
+ * n_events < MOE_N_STAGE_EVENTS; other errors as moe_fused_forward. */
 #define MOE_N_STAGE_EVENTS 8
-moe_status moe_debug_stage_events(void *const *events /*host*/, int32_t n_events);
+moe_status moe_fused_forward_timed(const moe_dims *dims /*host*/, const float *x,
+                                   const float *w_router, const float *router_bias,
+                                   const int32_t *k_per_token, const moe_weights *w /*host*/,
+                                   const float *logits_override, float *out,
+                                   int32_t *topk_ids_out, float *topk_w_out, void *workspace,
+                                   size_t workspace_bytes, void *const *stage_events /*host*/,
+                                   int32_t n_events, void *stream);
 
 const char *moe_status_str(moe_status s);
 const char *moe_last_error(void); /* thread-local detail of this thread's last failing call */

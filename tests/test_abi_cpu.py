@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.ABI_VERSION == 3
+    assert fp8.ABI_VERSION == 4
     assert fp8._status_str(0) == b"ok"
     assert fp8._status_str(ERR_WORKSPACE) == b"workspace too small"
     assert fp8._status_str(99) == b"unknown status"
@@ -107,12 +107,39 @@ def test_fused_forward_rejects_null_and_alignment_and_workspace():
     bad_flags = _dims()
     bad_flags.flags = 1 << 5
     assert call(dims=bad_flags) == ERR_UNSUPPORTED
+    # the fused combine is not built: refused, on every call that takes dims
+    fc = _dims()
+    fc.flags = fp8.MOE_F_FUSED_COMBINE
+    assert call(dims=fc) == ERR_UNSUPPORTED
+    assert b"MOE_F_FUSED_COMBINE" in fp8._last_error()
+    assert fp8.workspace_bytes(fc) == 0
+    cap = fp8.capacity(16, 8, 2, 16)
+    assert fp8._gate_up(C.byref(fc), cap, FAKE, FAKE, FAKE, FAKE, C.byref(w), FAKE, None) == ERR_UNSUPPORTED
+    assert fp8._combine(C.byref(fc), cap, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUPPORTED
     # the single-launch flag is switched off: refused before any launch
     for extra in (0, fp8.MOE_F_NO_REQUANT):
         pers = _dims()
         pers.flags = fp8.MOE_F_PERSISTENT | extra
         assert call(dims=pers) == ERR_UNSUPPORTED
         assert b"switched off" in fp8._last_error()
+
+
+def test_timed_forward_checks_its_events_and_keeps_no_pointer():
+    """moe_fused_forward_timed takes the stage events as an argument of the
+    call (the library keeps no caller pointer between calls) and refuses a
+    short event array before anything is enqueued."""
+    dm = _dims()
+    w = fp8._Weights(*([FAKE] * 12))
+    ev = (C.c_void_p * fp8.N_STAGE_EVENTS)(*([FAKE] * fp8.N_STAGE_EVENTS))
+    timed = lambda events, n, wsb=1 << 40: fp8._fused_forward_timed(
+        C.byref(dm), FAKE, FAKE, None, None, C.byref(w), None, FAKE, None, None, FAKE, wsb,
+        events, n, None)
+    assert timed(ev, fp8.N_STAGE_EVENTS - 1) == ERR_SHAPE
+    assert b"stage events" in fp8._last_error()
+    # with no events it validates exactly like moe_fused_forward
+    assert timed(None, 0, wsb=16) == ERR_WORKSPACE
+    assert timed(ev, fp8.N_STAGE_EVENTS, wsb=16) == ERR_WORKSPACE
+    assert not hasattr(C.CDLL(str(fp8.LIB_PATH)), "moe_debug_stage_events")
 
 
 def test_packed_weight_bytes_and_pack_validation():
