@@ -72,6 +72,8 @@ _last_error = _sig("moe_last_error", C.c_char_p)
 _abi_version = _sig("moe_abi_version", _i32)
 _fused_forward_timed = _sig("moe_fused_forward_timed", _i32, _DP, _vp, _vp, _vp, _vp, _WP, _vp,
                             _vp, _vp, _vp, _vp, C.c_size_t, C.POINTER(_vp), _i32, _vp)
+_fused_forward_noalloc = _sig("moe_fused_forward_noalloc", _i32, _DP, _vp, _vp, _vp, _vp, _WP,
+                              _vp, _vp, _vp, _vp, _vp)
 _group_tokens = _sig("moe_group_tokens", _i32, _vp, _i32, _i32, _i32, _i32, _vp)
 _k_tiers = _sig("moe_k_tiers", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 
@@ -79,6 +81,7 @@ N_STAGE_EVENTS = 8
 STAGES = ("route", "topk", "permute", "gate_up", "requant", "down", "combine")
 
 ABI_VERSION = int(_abi_version())
+STATIC_WORKSPACE_BYTES = 128 << 20  # MOE_STATIC_WORKSPACE_BYTES
 
 
 class MoEError(RuntimeError):
@@ -390,6 +393,20 @@ class MoELayer:
             C.byref(self._wstruct), _ptr(logits_override, torch.float32), _ptr(out),
             _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), _ptr(ws), ws.numel(), ev,
             0 if ev is None else len(stage_events), _stream(stream)))
+        return out
+
+    def forward_noalloc(self, x: torch.Tensor, out: torch.Tensor, k_per_token=None,
+                        logits_override=None, topk_ids=None, topk_w=None, stream=None):
+        """The same forward through moe_fused_forward_noalloc: the library's
+        own static device workspace, no allocation by the library or here
+        (out is the caller's).  Calls overlapping on one GPU race."""
+        T = x.shape[0]
+        dm = self.dims(T)
+        _check(_fused_forward_noalloc(
+            C.byref(dm), _ptr(x, torch.float32), _ptr(self.w_router, torch.float32),
+            _ptr(self.router_bias, torch.float32), _ptr(k_per_token, torch.int32),
+            C.byref(self._wstruct), _ptr(logits_override, torch.float32), _ptr(out, torch.float32),
+            _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), _stream(stream)))
         return out
 
     __call__ = forward

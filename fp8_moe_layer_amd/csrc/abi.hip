@@ -452,6 +452,42 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   return ok();
 }
 
+// Allocation-free entry point: the workspace lives in this file-scope device
+// array (one copy per GPU, held until the process ends).  Its device
+// address is taken once per device with hipGetSymbolAddress and kept; host
+// code never passes the array's own name to a kernel.
+}  // namespace
+
+// At most MOE_STATIC_WORKSPACE_BYTES; see the header.  File scope, internal
+// linkage: in host code `scratch` names a host-side stand-in, never passed to
+// a kernel or a copy -- only the address hipGetSymbolAddress returns is.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = MOE_STATIC_WORKSPACE_BYTES;
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+moe_status scratch_of_current_device(void **ptr, const char *fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device ordinal %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -671,6 +707,27 @@ moe_status moe_fused_forward_timed(const moe_dims *dims, const float *x, const f
   return enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
                          topk_ids_out, topk_w_out, static_cast<char *>(workspace), L,
                          reinterpret_cast<hipEvent_t const *>(stage_events), as_stream(stream));
+}
+
+moe_status moe_fused_forward_noalloc(const moe_dims *dims, const float *x, const float *w_router,
+                                     const float *router_bias, const int32_t *k_per_token,
+                                     const moe_weights *w, const float *logits_override,
+                                     float *out, int32_t *topk_ids_out, float *topk_w_out,
+                                     void *stream) {
+  const char *fn = "moe_fused_forward_noalloc";
+  moe_status s = check_forward(dims, x, w_router, w, logits_override, out, fn);
+  if (s) return s;
+  const Layout L = layout_of(dims);
+  if (L.total > kStaticScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "%s: these dims need %zu bytes of workspace, above the %zu-byte static scratch "
+                "array; use moe_fused_forward with a caller workspace",
+                fn, L.total, kStaticScratchBytes);
+  void *ws = nullptr;
+  if ((s = scratch_of_current_device(&ws, fn))) return s;
+  return enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
+                         topk_ids_out, topk_w_out, static_cast<char *>(ws), L, nullptr,
+                         as_stream(stream));
 }
 
 }  // extern "C"

@@ -244,6 +244,28 @@ moe_status moe_fused_forward(const moe_dims *dims /*host*/, const float *x, cons
                              float *out, int32_t *topk_ids_out, float *topk_w_out,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward pass as moe_fused_forward, with the workspace taken from a device
+ * array inside the library instead of a caller buffer.  The array,
+ * MOE_STATIC_WORKSPACE_BYTES, exists once per GPU the library runs on and
+ * is held until the process ends; its device address is looked up on the
+ * first call on each device.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); the caller still passes the inputs and
+ * outputs.  Dims whose workspace (moe_workspace_bytes) exceeds the array
+ * return MOE_ERR_WORKSPACE with nothing enqueued -- the decode-sized layers
+ * fit, prefill-sized ones need moe_fused_forward.  Nothing in the array has
+ * to start at zero (every stage writes what the next one reads).  Every call
+ * on one GPU shares that GPU's array: calls whose work overlaps on one GPU
+ * (other streams, other threads) race; serialise them.  Other arguments and
+ * errors as moe_fused_forward. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+moe_status moe_fused_forward_noalloc(const moe_dims *dims /*host*/, const float *x,
+                                     const float *w_router, const float *router_bias,
+                                     const int32_t *k_per_token, const moe_weights *w /*host*/,
+                                     const float *logits_override, float *out,
+                                     int32_t *topk_ids_out, float *topk_w_out, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */

@@ -142,6 +142,21 @@ def test_timed_forward_checks_its_events_and_keeps_no_pointer():
     assert not hasattr(C.CDLL(str(fp8.LIB_PATH)), "moe_debug_stage_events")
 
 
+def test_noalloc_forward_refuses_before_touching_the_device():
+    """moe_fused_forward_noalloc validates like moe_fused_forward and refuses
+    dims whose workspace exceeds the static array, all before any device
+    call (so these run without a GPU)."""
+    w = fp8._Weights(*([FAKE] * 12))
+    na = lambda dm, x=FAKE: fp8._fused_forward_noalloc(C.byref(dm), x, FAKE, None, None, C.byref(w),
+                                                       None, FAKE, None, None, None)
+    assert na(_dims(T=0)) == ERR_SHAPE
+    assert na(_dims(), x=None) == ERR_NULL
+    big = _dims(T=4096, d=2048, f=768, E=128, k_max=8)
+    assert fp8.workspace_bytes(big) > fp8.STATIC_WORKSPACE_BYTES
+    assert na(big) == ERR_WORKSPACE
+    assert b"static scratch" in fp8._last_error()
+
+
 def test_packed_weight_bytes_and_pack_validation():
     assert fp8.packed_weight_bytes(16, 64) == 16 * 128          # tail padded to a full tile
     assert fp8.packed_weight_bytes(32, 256) == 32 * 256
