@@ -340,8 +340,9 @@ class MoELayer:
     forward(x) runs the whole layer (quantise, router, top-k, permutation,
     gate/up + SiLU*up, requantisation, down projection, combine) in the
     library's kernels on the current stream -- six launches at decode sizes,
-    eight to ten at prefill sizes (persistent=True, one cooperative launch, is
-    refused).  The workspace is allocated once per token count and reused.
+    eight to ten at prefill sizes, or (persistent=True) one cooperative
+    launch after a one-wave reset.  The workspace is allocated once per
+    token count and reused.
     """
 
     def __init__(self, weights: DeviceWeights, w_router: Optional[torch.Tensor], k_max: int,
@@ -394,6 +395,15 @@ class MoELayer:
             _ptr(topk_ids, torch.int32), _ptr(topk_w, torch.float32), _ptr(ws), ws.numel(), ev,
             0 if ev is None else len(stage_events), _stream(stream)))
         return out
+
+    def status(self) -> int:
+        """The persistent launch's status word (workspace offset 0): 0 = ok,
+        1 = a grid barrier timed out.  Synchronises; meaningful only after a
+        forward with persistent=True."""
+        if not self.persistent or not self._ws:
+            return 0
+        ws = next(iter(self._ws.values()))
+        return int(ws[:4].view(torch.int32).item())
 
     def forward_noalloc(self, x: torch.Tensor, out: torch.Tensor, k_per_token=None,
                         logits_override=None, topk_ids=None, topk_w=None, stream=None):

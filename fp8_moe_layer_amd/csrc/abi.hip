@@ -271,7 +271,7 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
 
 // Workspace layout of moe_fused_forward (all pieces 256-byte aligned).
 struct Layout {
-  size_t xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
+  size_t bar, xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
       hq, sh, y, total;
   int32_t capacity, rows_total, max_items, row_chunk, msub, msub_big, splits;
   bool nt_gu, nt_dn;  // non-temporal weight loads
@@ -287,7 +287,9 @@ Layout layout_of(const moe_dims *d) {
   L.msub = choose_msub(d);
   L.gu = plan_gemm(d, L.msub, true);
   L.dn = plan_gemm(d, L.msub, false);
-  L.msub_big = (L.gu.nb == 2 && L.dn.nb == 2) ? choose_msub_big(d, L.msub) : L.msub;
+  const bool persistent = d->flags & MOE_F_PERSISTENT;
+  // the single launch runs one row-pass shape: items cut at 16*msub rows
+  L.msub_big = (L.gu.nb == 2 && L.dn.nb == 2 && !persistent) ? choose_msub_big(d, L.msub) : L.msub;
   L.row_chunk = 16 * L.msub_big;
   L.splits = L.dn.splits;
   {
@@ -305,6 +307,7 @@ Layout layout_of(const moe_dims *d) {
     o = up256(o + bytes);
     return at;
   };
+  L.bar = persistent ? take(kPersistBarBytes) : 0;  // first: the status word at offset 0
   L.xq = take(T * d->d);
   L.sx = take(T * 4);
   L.logits = take(T * d->E * 4);
@@ -347,11 +350,6 @@ moe_status check_forward(const moe_dims *dims, const float *x, const float *w_ro
                          const char *fn) {
   moe_status s = check_dims(dims, fn);
   if (s) return s;
-  // The single-launch path (kernels_persistent.hip) is switched off: under
-  // test on gfx950 its cooperative launch did not complete (the grid-wide
-  // barrier never released) and the cause is not established.
-  if (dims->flags & MOE_F_PERSISTENT)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: MOE_F_PERSISTENT is switched off in this build", fn);
   if ((s = check_weights(dims, w, fn))) return s;
   if (!x || !out) return fail(MOE_ERR_NULL, "%s: x and out are required", fn);
   if (!w_router && !logits_override)
@@ -389,6 +387,55 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], st);
   };
+
+  if (dims->flags & MOE_F_PERSISTENT) {
+    if (L.gu.nb != 2 || L.dn.nb != 2)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "moe_fused_forward: MOE_F_PERSISTENT runs two-operand GEMM tiles only");
+    const int32_t grid = persistent_grid(L.msub, device_cus());
+    if (grid < 1)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "moe_fused_forward: the single-launch kernel cannot keep one workgroup "
+                  "resident on every compute unit of this device");
+    PersistentLaunch p{};
+    p.rs = row_space(dims, L.capacity, sorted, offsets);
+    p.rs.items = items;
+    p.rs.n_items = n_items;
+    p.rs.max_items = L.max_items;
+    p.w = to_internal(w);
+    p.x = x;
+    p.w_router = w_router;
+    p.bias = router_bias;
+    p.kpt = k_per_token;
+    p.logits_override = logits_override;
+    p.logits = logits;
+    p.xq = xq;
+    p.sx = sx;
+    p.ids = ids;
+    p.tw = tw;
+    p.sorted = sorted;
+    p.offsets = offsets;
+    p.block_expert = block_expert;
+    p.inv = inv;
+    p.n_blocks = n_blocks;
+    p.items = items;
+    p.n_items = n_items;
+    p.h = h;
+    p.hq = hq;
+    p.sh = sh;
+    p.y = y;
+    p.out = out;
+    p.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
+    p.block_m = dims->block_m;
+    p.row_chunk = L.row_chunk;
+    p.msub = L.msub;
+    p.splits = requant ? L.splits : 1;
+    p.no_requant = !requant;
+    mark(0);
+    if ((s = hip_status(launch_persistent(p, grid, st), "persistent"))) return s;
+    for (int i = 1; i < MOE_N_STAGE_EVENTS; ++i) mark(i);
+    return ok();
+  }
 
   mark(0);
   const float *lg = logits_override;

@@ -123,9 +123,14 @@ hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, co
                           hipStream_t stream);
 
 // Everything the single-launch (persistent) layer needs: the same buffers
-// as the per-stage path.
+// as the per-stage path, plus the grid-barrier state (kPersistBarSlots
+// words, kPersistBarStride words apart; word 0 is the status word: 0 = ok,
+// 1 = a grid barrier timed out).
+constexpr int kPersistBarSlots = 34;
+constexpr int kPersistBarStride = 16384;  // 64 KB
+constexpr size_t kPersistBarBytes = (size_t)kPersistBarSlots * kPersistBarStride * sizeof(uint32_t);
 struct PersistentLaunch {
-  RowSpace rs;  // with the work list
+  RowSpace rs;  // with the work list (items cut at 16*msub rows)
   ExpertWeights w;
   const float *x, *w_router, *bias;
   const int32_t *kpt;
@@ -141,11 +146,15 @@ struct PersistentLaunch {
   float *h;
   uint8_t *hq;
   float *sh, *y, *out;
-  int32_t block_m, row_chunk, msub, splits;
+  uint32_t *bar;
+  int32_t block_m, row_chunk, msub, splits, no_requant;
 };
-// One cooperative launch; returns the launch error
-// (hipErrorCooperativeLaunchTooLarge when the grid cannot be resident).
-// Switched off: not called (see kernels_persistent.hip).
-hipError_t launch_persistent(const PersistentLaunch &p, hipStream_t stream);
+// Workgroups of the persistent grid for row passes of 16*msub rows (16: the
+// prefill tile) on a device of `cus` compute units: one per compute unit, or
+// 0 when the compiled kernel cannot keep one resident per compute unit.
+int32_t persistent_grid(int32_t msub, int32_t cus);
+// The barrier-state reset and the cooperative launch (grid from
+// persistent_grid); returns the launch error.
+hipError_t launch_persistent(const PersistentLaunch &p, int32_t grid, hipStream_t stream);
 
 }  // namespace fp8moe

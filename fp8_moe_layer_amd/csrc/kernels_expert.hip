@@ -100,64 +100,8 @@ __global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
     wsgemm_tile<ML, 2, GATEUP, NT>(g, blockIdx.x, abuf);
 }
 
-// ------------------------------------------------------------------ down, fp32 products
-// No-requant mode: y[row][c] = (sum_o h[row][o] dec(Wd[c][o])) * s_down[c] on
-// v_mfma_f32_16x16x4_f32.  Lane l (channel l%16, group kg = l/16) owns, of
-// each 128-wide K step, the indices [16kg, +16) and [64 + 16kg, +16) -- the
-// two 16-byte pieces of its weight tile -- and instruction q of the step
-// takes the q-th of them, for A and B alike.  An accuracy mode: simple
-// direct loads, no prefetch pipeline.
 __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
-  const RowSpace &rs = g.rs;
-  const int d = rs.d, f = rs.f;
-  const int KT = (f + 127) >> 7;
-  const int n_tiles = (d + 63) >> 6;
-  const int item_id = blockIdx.x / n_tiles;
-  const int tile = blockIdx.x - item_id * n_tiles;
-  int expert, row0, rows;
-  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
-  const bool shared = expert >= rs.E;
-  const size_t ex = (size_t)(shared ? expert - rs.E : expert);
-  const uint8_t *wd = (shared ? g.w.ws_down : g.w.w_down) + ex * d * (size_t)KT * 128;
-  const float *sd = (shared ? g.w.ss_down : g.w.s_down) + ex * d;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ln = lane & 15, kg = lane >> 4;
-  const int oc = (tile << 6) + (wave << 4) + ln;
-  const uint8_t *bp = wd + (size_t)((oc < d ? oc : d - 1) >> 4) * KT * 2048 + lane * 16;
-  const bool half_tail = (f & 127) != 0;
-  for (int r0 = 0; r0 < rows; r0 += 16) {
-    const int r = r0 + ln;
-    const bool aok = r < rows && row_real(rs, row0 + r);
-    const float *arow = g.a32 + (size_t)(row0 + (r < rows ? r : 0)) * f + kg * 16;
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < KT; ++ks) {
-      const bool hi_ok = !(half_tail && ks == KT - 1);  // K past f: zero weights, no A read
-      const v4i w0 = load16(bp + ks * 2048);
-      const v4i w1 = load16(bp + ks * 2048 + 1024);
-      const uint32_t ww[8] = {(uint32_t)w0.x, (uint32_t)w0.y, (uint32_t)w0.z, (uint32_t)w0.w,
-                              (uint32_t)w1.x, (uint32_t)w1.y, (uint32_t)w1.z, (uint32_t)w1.w};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        v4f av = {0.f, 0.f, 0.f, 0.f};
-        if (aok && (q < 4 || hi_ok))
-          av = *reinterpret_cast<const v4f *>(arow + ks * 128 + (q < 4 ? 4 * q : 64 + 4 * (q - 4)));
-        const v2f lo = e4m3x2_to_f32<false>(ww[q]);
-        const v2f hi = e4m3x2_to_f32<true>(ww[q]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, lo.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, lo.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, hi.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, hi.y, acc, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = r0 + kg * 4 + i;
-      if (rr < rows && oc < d) {
-        const int grow = row0 + rr;
-        g.out[(size_t)grow * d + oc] = row_real(rs, grow) ? acc[i] * sd[oc] : 0.0f;
-      }
-    }
-  }
+  down_f32_tile(g, blockIdx.x, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ weight tile order

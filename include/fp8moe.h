@@ -69,11 +69,20 @@ enum {
 enum {
   MOE_F_NO_REQUANT = 1u << 0, /* keep SiLU*up in fp32 and run the down projection on fp32
                                  products; an accuracy mode, not a fast path */
-  MOE_F_PERSISTENT = 1u << 1, /* reserved for running moe_fused_forward as one cooperative
-                                 launch (the fused single kernel of the Alpha-MoE article,
-                                 section "Comment fonctionne le megakernel").  Switched off in
-                                 this build: moe_fused_forward returns MOE_ERR_UNSUPPORTED
-                                 when it is set */
+  MOE_F_PERSISTENT = 1u << 1, /* run the whole layer as one resident-grid (cooperative)
+                                 launch, the stages separated by grid-wide barriers inside
+                                 the kernel (the fused persistent kernel of the Alpha-MoE
+                                 article, section "Comment fonctionne le megakernel"); a
+                                 one-wave kernel zeroing the barrier state precedes it.
+                                 Routing (ids, weights) is identical to the per-stage path;
+                                 outputs agree to rounding.  The workspace then starts with
+                                 the barrier state, and the int32 at byte offset 0 of the
+                                 workspace is a status word the caller may read after
+                                 synchronising: 0 = ok, 1 = a grid barrier timed out (every
+                                 wait is bounded, so a grid that cannot run co-resident ends
+                                 with this status instead of hanging; outputs are then
+                                 invalid).  MOE_ERR_UNSUPPORTED when the device cannot keep
+                                 one workgroup resident per compute unit */
   MOE_F_FUSED_COMBINE = 1u << 2 /* reserved for a combine fused into the down projection's
                                  epilogue.  Not built: with expert-major tiles the only fusion
                                  is a floating-point accumulation of each token's slots in

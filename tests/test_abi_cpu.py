@@ -116,12 +116,16 @@ def test_fused_forward_rejects_null_and_alignment_and_workspace():
     cap = fp8.capacity(16, 8, 2, 16)
     assert fp8._gate_up(C.byref(fc), cap, FAKE, FAKE, FAKE, FAKE, C.byref(w), FAKE, None) == ERR_UNSUPPORTED
     assert fp8._combine(C.byref(fc), cap, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUPPORTED
-    # the single-launch flag is switched off: refused before any launch
+    # the single-launch flag: its workspace adds the grid-barrier state (2.2 MB,
+    # the status word first); everything else is validated as for the staged path
     for extra in (0, fp8.MOE_F_NO_REQUANT):
         pers = _dims()
         pers.flags = fp8.MOE_F_PERSISTENT | extra
-        assert call(dims=pers) == ERR_UNSUPPORTED
-        assert b"switched off" in fp8._last_error()
+        stg = _dims()
+        stg.flags = extra
+        assert fp8.workspace_bytes(pers) >= fp8.workspace_bytes(stg) + 34 * 65536
+        assert call(dims=pers, x=None) == ERR_NULL
+        assert call(dims=pers, wsb=fp8.workspace_bytes(pers) - 1) == ERR_WORKSPACE
 
 
 def test_timed_forward_checks_its_events_and_keeps_no_pointer():
