@@ -276,12 +276,13 @@ class Shape:
                                          dw.ws_gate, dw.ws_up, dw.ss_gate, dw.ss_up, dw.ws_down,
                                          dw.ss_down)])
 
-    def layers(self, T, bias, no_requant=False):
+    def layers(self, T, bias, no_requant=False, persistent=False):
         """R rotated weight copies, R x (a step's active weight bytes) >= 1 GB
         (active experts counted from a first forward at this batch)."""
         import numpy as np
         torch, fp8, spec = self.torch, self.fp8, self.spec
-        base = fp8.MoELayer(self.dw, self.w_router, spec.k, bias, no_requant=no_requant)
+        base = fp8.MoELayer(self.dw, self.w_router, spec.k, bias, no_requant=no_requant,
+                            persistent=persistent)
         ids0 = torch.empty((T, spec.k), dtype=torch.int32, device=self.dev)
         base.forward(self.x[:T].contiguous(), k_per_token=self.kpt_of(T), topk_ids=ids0)
         i0 = ids0.cpu().numpy()
@@ -290,8 +291,8 @@ class Shape:
         copies = max(1, min(16, math.ceil(1e9 / (active * expert_bytes))))
         while len(self._copies) < copies - 1:
             self._copies.append(self.clone())
-        return [base] + [fp8.MoELayer(c, self.w_router, spec.k, bias, no_requant=no_requant)
-                         for c in self._copies[:copies - 1]]
+        return [base] + [fp8.MoELayer(c, self.w_router, spec.k, bias, no_requant=no_requant,
+                                      persistent=persistent) for c in self._copies[:copies - 1]]
 
     def kpt_of(self, T):
         return None if self.kpt is None else self.kpt[:T].contiguous()
@@ -368,6 +369,21 @@ def parity_sample(shape, T, x, kpt, bias_np, out, ids, n):
             "ids_equal": bool(np.array_equal(ids[:n].cpu().numpy(), ido)), "tokens": n}
 
 
+def time_persistent(torch, shape, T, bias, x, kpt, steps, warmup, sh):
+    """The same steps as one cooperative launch each (MOE_F_PERSISTENT)."""
+    spec = shape.spec
+    lays = shape.layers(T, bias, persistent=True)
+    out = torch.empty((T, spec.d), dtype=torch.float32, device=shape.dev)
+    ids = torch.empty((T, spec.k), dtype=torch.int32, device=shape.dev)
+    ms = time_steps(torch, lays, x, kpt, out, ids, steps, warmup, sh)
+    status = max(lay.status() for lay in lays)
+    # phase boundaries of the last launch on the first copy (its own clock)
+    lays[0].forward(x, k_per_token=kpt, out=out, topk_ids=ids)
+    torch.cuda.synchronize()
+    return {"us_mean": round(ms * 1e3, 2), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "status": status, "phase_ends_us": lays[0].persistent_stamps()}
+
+
 def measure_point(torch, fp8, shape, T, bias, steps, warmup, sh, parity_n, label):
     """Time one layer shape at batch T; roofline fractions of the layer."""
     spec = shape.spec
@@ -400,12 +416,13 @@ def measure_point(torch, fp8, shape, T, bias, steps, warmup, sh, parity_n, label
         t = stages["down"] * 1e-6
         pt["down"] = {"us": stages["down"], "hbm_frac": round(acc["down_bytes"] / t / PEAK_HBM, 4),
                       "mfma_frac": round(acc["down_flops"] / t / PEAK_FP8, 4)}
+    pt["persistent"] = time_persistent(torch, shape, T, bias, x, kpt, steps, warmup, sh)
     if parity_n:
         bias_np = None if bias is None else bias.cpu().numpy()
         pt["parity"] = parity_sample(shape, T, x, kpt, bias_np, out, ids, parity_n)
     log(f"{label}: {pt['us_mean']} us (median {pt['us_median']}), D={acc['distinct_experts']}, "
         f"hbm {pt['hbm_frac']}, mfma {pt['mfma_frac']}, stages {stages}, "
-        f"parity {pt.get('parity')}")
+        f"persistent {pt['persistent']}, parity {pt.get('parity')}")
     del layers
     return pt, ms, dist, stages, acc, out, ids
 
@@ -512,6 +529,13 @@ def main():
              "mfma_frac_median": round(acc["layer_flops"] / med / PEAK_FP8, 5),
              "alg_bytes_note": "weights + scales of the distinct active and shared experts, "
                                "fp32 router weight, x read and out written (fp32)"}
+
+    # ---- the same steps as one persistent cooperative launch each
+    persistent = None
+    if not args.no_requant:
+        persistent = time_persistent(torch, shape, T, bias, x, kpt, args.steps, args.warmup, sh)
+        persistent["staged_us_mean"] = round(ms * 1e3, 2)
+        log(f"persistent single launch: {persistent}")
 
     # ---- the same steps replayed from HIP graphs (launch overhead removed)
     graph = None
@@ -759,6 +783,7 @@ def main():
         "step_us": step_us,
         "stages_us": stages_us,
         **({"graph": graph} if graph else {}),
+        **({"persistent": persistent} if persistent else {}),
         "parity": parity,
     }
     if points is not None:

@@ -405,6 +405,18 @@ class MoELayer:
         ws = next(iter(self._ws.values()))
         return int(ws[:4].view(torch.int32).item())
 
+    def persistent_stamps(self):
+        """Microseconds from the persistent launch's start to each of its
+        recorded phase boundaries (workgroup 0's clock: after each grid
+        barrier, then the end).  Synchronises; after a persistent forward."""
+        if not self.persistent or not self._ws:
+            return []
+        ws = next(iter(self._ws.values()))
+        off = 34 * 65536  # the stamps slot of the barrier state
+        st = ws[off:off + 80].view(torch.int64).cpu().tolist()
+        t0 = st[0]
+        return [round((v - t0) / 100.0, 2) for v in st[1:] if v >= t0 and v - t0 < 10**9]
+
     def forward_noalloc(self, x: torch.Tensor, out: torch.Tensor, k_per_token=None,
                         logits_override=None, topk_ids=None, topk_w=None, stream=None):
         """The same forward through moe_fused_forward_noalloc: the library's

@@ -125,8 +125,11 @@ hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, co
 // Everything the single-launch (persistent) layer needs: the same buffers
 // as the per-stage path, plus the grid-barrier state (kPersistBarSlots
 // words, kPersistBarStride words apart; word 0 is the status word: 0 = ok,
-// 1 = a grid barrier timed out).
-constexpr int kPersistBarSlots = 34;
+// 1 = a grid barrier timed out; the last slot holds workgroup 0's
+// s_memrealtime stamps at the kernel's start, after each grid barrier and at
+// its end, kPersistStamps of them).
+constexpr int kPersistBarSlots = 35;
+constexpr int kPersistStamps = 10;
 constexpr int kPersistBarStride = 16384;  // 64 KB
 constexpr size_t kPersistBarBytes = (size_t)kPersistBarSlots * kPersistBarStride * sizeof(uint32_t);
 struct PersistentLaunch {

@@ -56,9 +56,9 @@ constexpr int kPThreads = kPWaves * kWave;
 constexpr int kBarGroups = 16;
 constexpr int kXcds = 8;
 constexpr int kSlotStatus = 0, kSlotTop = 1, kSlotGroup = 2, kSlotXgen = kSlotGroup + kBarGroups,
-              kSlotXrdy = kSlotXgen + kXcds;
+              kSlotXrdy = kSlotXgen + kXcds, kSlotStamps = kSlotXrdy + kXcds;
 constexpr uint64_t kBarTimeoutTicks = 100000000ull;  // 1 s of the 100 MHz s_memrealtime clock
-static_assert(kSlotXrdy + kXcds <= kPersistBarSlots, "barrier slots");
+static_assert(kSlotStamps + 1 <= kPersistBarSlots, "barrier slots");
 
 __device__ __forceinline__ uint32_t *bar_slot(uint32_t *bar, int s) {
   return bar + (size_t)s * kPersistBarStride;
@@ -75,6 +75,12 @@ __device__ __forceinline__ bool wait_ge(uint32_t *p, uint32_t target, uint64_t t
     __builtin_amdgcn_s_sleep(1);
   }
   return true;
+}
+
+// Workgroup 0 records the 100 MHz clock at phase boundaries (stamp i).
+__device__ __forceinline__ void stamp(uint32_t *bar, int i) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && i < kPersistStamps)
+    reinterpret_cast<uint64_t *>(bar_slot(bar, kSlotStamps))[i] = __builtin_amdgcn_s_memrealtime();
 }
 
 __device__ __forceinline__ uint32_t xcc_id() {
@@ -167,6 +173,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
   const int lane = threadIdx.x & 63;
   const int T = rs.T, d = rs.d, E = rs.E, K = rs.k_max;
   uint32_t gen = 0;
+  stamp(a.bar, 0);
 
   // ---- route: logits (+ quantised x, + top-k) with the per-stage arithmetic
   const float *lg = a.logits_override ? a.logits_override : a.logits;
@@ -209,12 +216,14 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
     }
   }
   if (!grid_barrier(a.bar, ++gen, &flag)) return;
+  stamp(a.bar, gen);
 
   // ---- top-k and routing weights
   if (!topk_done) {
     for (int t = B * kPWaves + wave; t < T; t += G * kPWaves)
       topk_token_wave(lg, T, E, K, a.kpt, a.ids, a.tw, t, lane);
     if (!grid_barrier(a.bar, ++gen, &flag)) return;
+  stamp(a.bar, gen);
   }
 
   // ---- permutation and work list (one workgroup)
@@ -223,6 +232,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
                            a.block_expert, a.inv, a.n_blocks, a.items, a.n_items, a.row_chunk, T,
                            rs.S, reinterpret_cast<int *>(lds));
   if (!grid_barrier(a.bar, ++gen, &flag)) return;
+  stamp(a.bar, gen);
 
   // ---- gate/up grouped GEMM + SiLU*up
   {
@@ -243,6 +253,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
     }
   }
   if (!grid_barrier(a.bar, ++gen, &flag)) return;
+  stamp(a.bar, gen);
 
   // ---- per-row requantisation of h
   const int rows_total = rs.capacity + rs.S * T;
@@ -257,6 +268,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
       }
     }
     if (!grid_barrier(a.bar, ++gen, &flag)) return;
+  stamp(a.bar, gen);
   }
 
   // ---- down grouped GEMM (K splits into separate slabs)
@@ -285,6 +297,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
     }
   }
   if (!grid_barrier(a.bar, ++gen, &flag)) return;
+  stamp(a.bar, gen);
 
   // ---- weighted combine
   {
@@ -294,6 +307,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
       combine_chunk<kPThreads>(rs, a.y, a.no_requant ? 1 : a.splits, a.ids, a.tw, a.inv, a.out,
                                task / nc, (task % nc) * chunk);
   }
+  stamp(a.bar, kPersistStamps - 1);
 }
 
 // Zeroes the barrier state and the status word before a launch.
