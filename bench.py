@@ -427,6 +427,65 @@ def measure_point(torch, fp8, shape, T, bias, steps, warmup, sh, parity_n, label
     return pt, ms, dist, stages, acc, out, ids
 
 
+def _capture(torch, lay, x, kpt, out, ids):
+    cap = torch.cuda.Stream()  # default priority
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        lay.forward(x, k_per_token=kpt, out=out, topk_ids=ids)  # workspace before capture
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lay.forward(x, k_per_token=kpt, out=out, topk_ids=ids)
+    return g
+
+
+def _time_replays(torch, gs, steps, warmup):
+    for i in range(warmup):
+        gs[i % len(gs)].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        gs[i % len(gs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def graph_timings(torch, fp8, shape, layers, x, kpt, out, ids, eager_ms, T, args, sh):
+    """The layer replayed from HIP graphs.  For the elastic-k shape, one graph
+    per routing budget k (the MoE-Prism segmented executor's per-k MoE
+    segments): each k timed as graph replay, eager launches and the single
+    persistent launch over the same batch; otherwise one graph per weight
+    copy of the measured batch."""
+    spec = shape.spec
+    if spec.name != "prism":
+        gs = [_capture(torch, lay, x, kpt, out, ids) for lay in layers]
+        gms = _time_replays(torch, gs, args.steps, args.warmup)
+        del gs
+        res = {"us_per_step": round(gms * 1e3, 2), "eager_us_per_step": round(eager_ms * 1e3, 2),
+               "tokens_per_s": round(T / (gms * 1e-3), 1), "graphs": len(layers)}
+        log(f"graph replay: {res}")
+        return res
+    per_k = []
+    for k in (4, 8, 16, 32):
+        lay = fp8.MoELayer(shape.dw, shape.w_router, k)
+        ok = torch.empty((T, spec.d), dtype=torch.float32, device=shape.dev)
+        ik = torch.empty((T, k), dtype=torch.int32, device=shape.dev)
+        g = _capture(torch, lay, x, None, ok, ik)
+        gms = _time_replays(torch, [g], args.steps, args.warmup)
+        del g
+        ems = time_steps(torch, [lay], x, None, ok, ik, args.steps, args.warmup, sh)
+        pl = fp8.MoELayer(shape.dw, shape.w_router, k, persistent=True)
+        pms = time_steps(torch, [pl], x, None, ok, ik, args.steps, args.warmup, sh)
+        ent = {"k": k, "graph_us": round(gms * 1e3, 2), "eager_us": round(ems * 1e3, 2),
+               "persistent_us": round(pms * 1e3, 2), "persistent_status": pl.status()}
+        per_k.append(ent)
+        log(f"graph per k: {ent}")
+    return {"per_k": per_k, "T": T, "note": "one captured graph per k, all tokens served at k"}
+
+
 def bias_for(wl, cfg, T, distinct, seed, dev):
     """Router bias of a layer shape at batch T, on the device (or None)."""
     if cfg == "deepseek":
@@ -540,32 +599,7 @@ def main():
     # ---- the same steps replayed from HIP graphs (launch overhead removed)
     graph = None
     if args.graph:
-        gs = []
-        cap = torch.cuda.Stream()  # default priority
-        for lay in layers:
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                lay.forward(x, k_per_token=kpt, out=out, topk_ids=ids)
-            torch.cuda.current_stream().wait_stream(cap)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                lay.forward(x, k_per_token=kpt, out=out, topk_ids=ids)
-            gs.append(g)
-        for i in range(args.warmup):
-            gs[i % len(gs)].replay()
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for i in range(args.steps):
-            gs[i % len(gs)].replay()
-        end.record()
-        torch.cuda.synchronize()
-        gms = start.elapsed_time(end) / args.steps
-        graph = {"us_per_step": round(gms * 1e3, 2), "eager_us_per_step": round(ms * 1e3, 2),
-                 "tokens_per_s": round(T / (gms * 1e-3), 1), "graphs": len(gs)}
-        log(f"graph replay: {graph}")
-        del gs
+        graph = graph_timings(torch, fp8, shape, layers, x, kpt, out, ids, ms, T, args, sh)
 
     # ---- decode batches from a token pool: arrival order vs grouped by expert affinity
     grouping = None
