@@ -222,7 +222,8 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
   const int N = gate_up ? d->f : d->d;
   const int K = gate_up ? d->d : d->f;
   const double rows = (double)d->T * d->k_max + (double)d->n_shared * d->T;
-  const int forced = env_int("FP8MOE_WAVES", 0);            // tile-tuning overrides
+  const int forced_dn = gate_up ? 0 : env_int("FP8MOE_DOWN_WAVES", 0);  // tile-tuning overrides
+  const int forced = forced_dn > 0 ? forced_dn : env_int("FP8MOE_WAVES", 0);
   const int forced_nb = env_int("FP8MOE_NB", 0);
   const int forced_splits = env_int("FP8MOE_DOWN_SPLITS", 0);
   const bool can_split = !gate_up && !(d->flags & MOE_F_NO_REQUANT);
@@ -323,7 +324,8 @@ Layout layout_of(const moe_dims *d) {
   L.h = take(R * d->f * 4);
   L.hq = take(R * d->f);
   L.sh = take(R * 4);
-  L.y = take((size_t)L.splits * R * d->d * 4);
+  // the fused path keeps y in fp16 (fp32 in the no-requant accuracy mode)
+  L.y = take((size_t)L.splits * R * d->d * ((d->flags & MOE_F_NO_REQUANT) ? 4 : 2));
   L.total = o;
   return L;
 }
@@ -384,6 +386,7 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   float *sh = reinterpret_cast<float *>(ws + L.sh);
   float *y = reinterpret_cast<float *>(ws + L.y);
   const bool requant = !(dims->flags & MOE_F_NO_REQUANT);
+  _Float16 *y16 = requant ? reinterpret_cast<_Float16 *>(ws + L.y) : nullptr;
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], st);
   };
@@ -424,6 +427,7 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
     p.hq = hq;
     p.sh = sh;
     p.y = y;
+    p.y16 = y16;
     p.out = out;
     p.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
     p.block_m = dims->block_m;
@@ -485,16 +489,16 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, y, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
+    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, nullptr, y16, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
                         "down")))
       return s;
   } else {
     mark(5);
-    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, false, st), "down")))
+    if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, nullptr, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, false, st), "down")))
       return s;
   }
   mark(6);
-  if ((s = hip_status(launch_combine(rs, y, L.splits, ids, tw, inv, out, st), "combine"))) return s;
+  if ((s = hip_status(launch_combine(rs, y, y16, L.splits, ids, tw, inv, out, st), "combine"))) return s;
   mark(7);
   return ok();
 }
@@ -695,7 +699,7 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
   int32_t sp, ks;
   down_split_geometry(dims->f, msub, 1, &sp, &ks);
   const bool nt = !f32 && dp.nb == 2 && msub <= 8 && stream_weights(dims, mbig, ks);
-  s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y,
+  s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y, nullptr,
                              msub, mbig, 1, dp.waves, dp.nb, nt, as_stream(stream)),
                  fn);
   return s ? s : ok();
@@ -714,7 +718,7 @@ moe_status moe_combine(const moe_dims *dims, int32_t capacity, const float *y,
   if ((int64_t)capacity < capacity_of(dims->T, dims->E, dims->k_max, dims->block_m))
     return fail(MOE_ERR_SHAPE, "%s: capacity=%d too small", fn, capacity);
   RowSpace rs = row_space(dims, capacity, nullptr, nullptr);
-  s = hip_status(launch_combine(rs, y, 1, topk_ids, topk_w, inv_pairs, out, as_stream(stream)), fn);
+  s = hip_status(launch_combine(rs, y, nullptr, 1, topk_ids, topk_w, inv_pairs, out, as_stream(stream)), fn);
   return s ? s : ok();
 }
 

@@ -52,6 +52,9 @@ struct GemmArgs {
   float *out;            // h [rows][f] or y [splits][rows][d]
   int32_t splits;        // K splits (down only; partial sums go to separate y slabs)
   int32_t ksplit;        // bytes of K per split (multiple of the chunk size)
+  // Down projection: when set, y is written here in fp16 (same layout; values
+  // beyond +-65504 saturate) instead of fp32 to `out`.
+  _Float16 *out16 = nullptr;
   // Decode down projection: tile t of expert e starts its K loop at step
   // ((t + 5e) * krot) % nks and wraps (0: no rotation).  When all of a
   // launch's workgroups run in one round they otherwise walk their weight
@@ -252,7 +255,43 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
       }
     }
   } else {
-    float *yp = g.out + (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
+    const size_t yoff = (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
+    if (g.out16) {
+      // fp16 y: lanes ln and ln^1 hold channels c, c+1 of a row; the even lane
+      // stores both as one 32-bit word (the odd lane's value comes over DPP,
+      // in every lane before any store condition).  A wave covers 64 bytes of
+      // a row, half a cache line: ordinary stores, so L2 merges the two
+      // halves before they go to memory.
+      _Float16 *yh = g.out16 + yoff;
+      const bool even = (lane & 1) == 0;
+      const bool live_nt = __builtin_amdgcn_ballot_w64(wo.ch[NB - 1] >= N) == 0;
+      size_t yrow = 0;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) {
+        if (m < msub) {
+          const v4f sh4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+          const int rlim = full ? 4 : prow - (m * 16 + kg * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              const float v = fminf(fmaxf(acc[m][nb][i] * sh4[i] * wo.wsc[nb], -65504.0f), 65504.0f);
+              const float u = dpp_mov<kDppQuadXor1>(v);
+              if (even && (m < msub - 1 || i < rlim) && (live_nt || wo.ch[nb] < N)) {
+                const v2h pk = {(_Float16)v, (_Float16)u};
+                *reinterpret_cast<v2h *>(yh + yrow + wo.ch[nb]) = pk;
+              }
+            }
+            yrow += i < 3 ? N : 13 * N;
+          }
+        }
+      }
+      return;
+    }
+    float *yp = g.out + yoff;
+    // one y element (non-temporal: a wave covers a whole 128-byte line of a row)
+    auto put = [&](float v, size_t at) { __builtin_nontemporal_store(v, yp + at); };
+    size_t yrow = 0;  // offset of the current row from yp
     // every lane's channels inside N (all but a partial last tile): no
     // per-store channel mask
     const bool live = __builtin_amdgcn_ballot_w64(wo.ch[NB - 1] >= N) == 0;
@@ -263,9 +302,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wo.wsc[nb], yp + wo.ch[nb]);
-          yp += i < 3 ? N : 13 * N;
+          for (int nb = 0; nb < NB; ++nb) put(acc[m][nb][i] * sh4[i] * wo.wsc[nb], yrow + wo.ch[nb]);
+          yrow += i < 3 ? N : 13 * N;
         }
       }
     } else {
@@ -279,10 +317,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
             if (m < msub - 1 || i < rlim) {
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb)
-                if (wo.ch[nb] < N)
-                  __builtin_nontemporal_store(acc[m][nb][i] * sh4[i] * wo.wsc[nb], yp + wo.ch[nb]);
+                if (wo.ch[nb] < N) put(acc[m][nb][i] * sh4[i] * wo.wsc[nb], yrow + wo.ch[nb]);
             }
-            yp += i < 3 ? N : 13 * N;
+            yrow += i < 3 ? N : 13 * N;
           }
         }
       }
@@ -795,14 +832,48 @@ __device__ __forceinline__ void requant_row_wave(const RowSpace &rs, const float
 // Slots are taken G at a time: their lookups (ids, inv, w) are requested
 // together, then every K-split piece of their rows (up to SM splits), then
 // the pieces are added in order -- two memory latencies per group.
-template <int G, int SM>
-__device__ __forceinline__ v4f combine_groups(const RowSpace &rs, const float *__restrict__ y,
-                                              int splits, const int32_t *__restrict__ ids,
-                                              const float *__restrict__ w,
-                                              const int32_t *__restrict__ inv, int t, int c) {
+// V consecutive y elements as floats: 16-byte loads (4 fp32 or 8 fp16).
+template <int V>
+struct Cols {
+  v4f v[V / 4];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) v[q] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void add(const Cols &o) {
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) v[q] += o.v[q];
+  }
+  __device__ __forceinline__ void fma(float w, const Cols &o) {
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) v[q] += w * o.v[q];
+  }
+};
+template <typename Y>
+constexpr int cols_per_load() { return 4; }
+
+__device__ __forceinline__ Cols<4> load_cols(const float *p) {
+  Cols<4> c;
+  c.v[0] = *reinterpret_cast<const v4f *>(p);
+  return c;
+}
+__device__ __forceinline__ Cols<4> load_cols(const _Float16 *p) {
+  typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+  const v4h h = *reinterpret_cast<const v4h *>(p);
+  Cols<4> c;
+  c.v[0] = v4f{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  return c;
+}
+
+template <int G, int SM, typename Y>
+__device__ __forceinline__ Cols<cols_per_load<Y>()> combine_groups(
+    const RowSpace &rs, const Y *__restrict__ y, int splits, const int32_t *__restrict__ ids,
+    const float *__restrict__ w, const int32_t *__restrict__ inv, int t, int c) {
+  constexpr int V = cols_per_load<Y>();
   const int d = rs.d, K = rs.k_max, J = K + rs.S;  // routed slots, then the shared rows
   const size_t slab = (size_t)(rs.capacity + rs.S * rs.T) * d;
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  Cols<V> acc;
+  acc.zero();
   for (int j0 = 0; j0 < J; j0 += G) {
     int row[G];
     float wt[G];
@@ -822,38 +893,43 @@ __device__ __forceinline__ v4f combine_groups(const RowSpace &rs, const float *_
         row[u] = j < J ? rs.capacity + (j - K) * rs.T + t : 0;
       }
     }
-    v4f v[G][SM];
+    Cols<V> v[G][SM];
 #pragma unroll
     for (int u = 0; u < G; ++u)
 #pragma unroll
       for (int sp = 0; sp < SM; ++sp)  // uniform conditions
-        if (j0 + u < J && sp < splits)
-          v[u][sp] = *reinterpret_cast<const v4f *>(y + sp * slab + (size_t)row[u] * d + c);
+        if (j0 + u < J && sp < splits) v[u][sp] = load_cols(y + sp * slab + (size_t)row[u] * d + c);
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       if (j0 + u < J) {
-        v4f cur = v[u][0];
+        Cols<V> cur = v[u][0];
 #pragma unroll
         for (int sp = 1; sp < SM; ++sp)
-          if (sp < splits) cur += v[u][sp];
-        if (ok[u]) acc += wt[u] * cur;
+          if (sp < splits) cur.add(v[u][sp]);
+        if (ok[u]) acc.fma(wt[u], cur);
       }
     }
   }
   return acc;
 }
 
-template <int NT>
-__device__ __forceinline__ void combine_chunk(const RowSpace &rs, const float *__restrict__ y,
+// Columns [c0, c0 + NT * cols_per_load<Y>()) of token t.
+template <int NT, typename Y>
+__device__ __forceinline__ void combine_chunk(const RowSpace &rs, const Y *__restrict__ y,
                                               int splits, const int32_t *__restrict__ ids,
                                               const float *__restrict__ w,
                                               const int32_t *__restrict__ inv,
                                               float *__restrict__ out, int t, int c0) {
-  const int c = c0 + threadIdx.x * 4;
+  constexpr int V = cols_per_load<Y>();
+  const int c = c0 + threadIdx.x * V;
   if (c >= rs.d) return;
-  const v4f acc = splits <= 2 ? combine_groups<8, 2>(rs, y, splits, ids, w, inv, t, c)
-                              : combine_groups<2, kMaxDownSplits>(rs, y, splits, ids, w, inv, t, c);
-  *reinterpret_cast<v4f *>(out + (size_t)t * rs.d + c) = acc;
+  // registers for the loads of a slot group: G slots x SM split pieces
+  const Cols<V> acc = splits == 1  ? combine_groups<8, 1>(rs, y, splits, ids, w, inv, t, c)
+                      : splits <= 2 ? combine_groups<8, 2>(rs, y, splits, ids, w, inv, t, c)
+                                    : combine_groups<2, kMaxDownSplits>(rs, y, splits, ids, w, inv, t, c);
+#pragma unroll
+  for (int q = 0; q < V / 4; ++q)
+    *reinterpret_cast<v4f *>(out + (size_t)t * rs.d + c + 4 * q) = acc.v[q];
 }
 
 }  // namespace fp8moe

@@ -105,11 +105,12 @@ hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float
 // Down projection from hq/sh, or (h32 != nullptr) straight from fp32 h with
 // fp32 products.  `splits` > 1 cuts K = f into that many ranges (fewer if f
 // is short) whose partial sums go to separate y slabs [split][rows][d]; the
-// count actually used is down_splits_used(f, msub, splits).
+// count actually used is down_splits_used(f, msub, splits).  y16 (hq/sh
+// input only): y written in fp16 there instead of fp32 to y.
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
-                       const ExpertWeights &w, float *y, int32_t msub, int32_t msub_big,
-                       int32_t splits, int32_t waves, int32_t nb, bool stream_weights,
-                       hipStream_t stream);
+                       const ExpertWeights &w, float *y, _Float16 *y16, int32_t msub,
+                       int32_t msub_big, int32_t splits, int32_t waves, int32_t nb,
+                       bool stream_weights, hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
 // Final K-split count and bytes per split for a requested split count.
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
@@ -117,9 +118,9 @@ void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *sp
 constexpr int kDownChannelsPerWave = 32;  // output channels per down-projection wave (nb 2)
 constexpr int kMaxDownSplits = 8;         // K splits of the down projection (y slabs)
 // out from y slabs summed in split order (splits <= kMaxDownSplits, else
-// hipErrorInvalidValue).
-hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
-                          const float *w, const int32_t *inv_pairs, float *out,
+// hipErrorInvalidValue); y16 != nullptr: the slabs are fp16 there.
+hipError_t launch_combine(const RowSpace &rs, const float *y, const _Float16 *y16, int32_t splits,
+                          const int32_t *ids, const float *w, const int32_t *inv_pairs, float *out,
                           hipStream_t stream);
 
 // Everything the single-launch (persistent) layer needs: the same buffers
@@ -149,6 +150,7 @@ struct PersistentLaunch {
   float *h;
   uint8_t *hq;
   float *sh, *y, *out;
+  _Float16 *y16;  // y in fp16 (requantised path), else nullptr
   uint32_t *bar;
   int32_t block_m, row_chunk, msub, splits, no_requant;
 };

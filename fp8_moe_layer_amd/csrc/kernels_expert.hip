@@ -142,12 +142,14 @@ __global__ __launch_bounds__(kRowThreads) void requant_kernel(RowSpace rs, const
 }
 
 // ------------------------------------------------------------------ combine
-__global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const float *__restrict__ y,
+template <typename Y>
+__global__ __launch_bounds__(256) void combine_kernel(RowSpace rs, const Y *__restrict__ y,
                                                       int splits, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv,
                                                       float *__restrict__ out) {
-  combine_chunk<256>(rs, y, splits, ids, w, inv, out, blockIdx.x, blockIdx.y * 1024);
+  combine_chunk<256>(rs, y, splits, ids, w, inv, out, blockIdx.x,
+                     blockIdx.y * 256 * cols_per_load<Y>());
 }
 
 // ------------------------------------------------------------------ launchers
@@ -270,9 +272,9 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits) {
 }
 
 hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, const float *h32,
-                       const ExpertWeights &w, float *y, int32_t msub, int32_t msub_big,
-                       int32_t splits, int32_t waves, int32_t nb, bool stream_weights,
-                       hipStream_t stream) {
+                       const ExpertWeights &w, float *y, _Float16 *y16, int32_t msub,
+                       int32_t msub_big, int32_t splits, int32_t waves, int32_t nb,
+                       bool stream_weights, hipStream_t stream) {
   if (h32) {
     GemmArgs g{rs, nullptr, nullptr, h32, w, y, 1, rs.f};
     const int blocks = grid_items(rs) * ((rs.d + 63) >> 6);
@@ -283,6 +285,7 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
   int32_t ksplit;
   down_split_geometry(rs.f, msub, splits, &splits, &ksplit);
   GemmArgs g{rs, hq, sh, nullptr, w, y, splits, ksplit};
+  g.out16 = y16;
   // 128-row passes and up (one round of workgroups at decode sizes): rotated
   // K starts, measured 95.6 -> 89.9 us at a Mixtral-shaped T=256 batch (the
   // shorter passes of smaller batches measured a little slower with it)
@@ -300,13 +303,17 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
                         : launch_nb2<false, false>(g, msub, msub_big, waves, stream);
 }
 
-hipError_t launch_combine(const RowSpace &rs, const float *y, int32_t splits, const int32_t *ids,
-                          const float *w, const int32_t *inv_pairs, float *out,
+hipError_t launch_combine(const RowSpace &rs, const float *y, const _Float16 *y16, int32_t splits,
+                          const int32_t *ids, const float *w, const int32_t *inv_pairs, float *out,
                           hipStream_t stream) {
   if (splits < 1 || splits > kMaxDownSplits) return hipErrorInvalidValue;
   if (rs.T == 0) return hipSuccess;
-  combine_kernel<<<dim3(rs.T, (rs.d + 1023) / 1024), 256, 0, stream>>>(rs, y, splits, ids, w,
-                                                                      inv_pairs, out);
+  if (y16)
+    combine_kernel<_Float16><<<dim3(rs.T, (rs.d + 1023) / 1024), 256, 0, stream>>>(
+        rs, y16, splits, ids, w, inv_pairs, out);
+  else
+    combine_kernel<float><<<dim3(rs.T, (rs.d + 1023) / 1024), 256, 0, stream>>>(
+        rs, y, splits, ids, w, inv_pairs, out);
   return hipGetLastError();
 }
 

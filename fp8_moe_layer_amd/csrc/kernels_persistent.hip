@@ -147,6 +147,7 @@ struct PersistArgs {
   float *h;
   uint8_t *hq;
   float *sh, *y, *out;
+  _Float16 *y16;
   uint32_t *bar;
   int32_t block_m, row_chunk, splits, ksplit, krot;
   int32_t no_requant;
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
   } else {
     GemmArgs g{rs, a.hq, a.sh, nullptr, a.w, a.y, a.splits, a.ksplit};
     g.krot = a.krot;
+    g.out16 = a.y16;
     if constexpr (PF) {
       const int n = rs.max_items * ((d + kPfWaves * 32 - 1) / (kPfWaves * 32)) * a.splits;
       for (int b = B; b < n; b += G) {
@@ -300,12 +302,18 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
   stamp(a.bar, gen);
 
   // ---- weighted combine
-  {
-    const int chunk = kPThreads * 4;
+  if (a.y16) {
+    const int chunk = kPThreads * cols_per_load<_Float16>();
     const int nc = (d + chunk - 1) / chunk;
     for (int task = B; task < T * nc; task += G)
-      combine_chunk<kPThreads>(rs, a.y, a.no_requant ? 1 : a.splits, a.ids, a.tw, a.inv, a.out,
-                               task / nc, (task % nc) * chunk);
+      combine_chunk<kPThreads>(rs, a.y16, a.splits, a.ids, a.tw, a.inv, a.out, task / nc,
+                               (task % nc) * chunk);
+  } else {
+    const int chunk = kPThreads * cols_per_load<float>();
+    const int nc = (d + chunk - 1) / chunk;
+    for (int task = B; task < T * nc; task += G)
+      combine_chunk<kPThreads>(rs, a.y, 1, a.ids, a.tw, a.inv, a.out, task / nc,
+                               (task % nc) * chunk);
   }
   stamp(a.bar, kPersistStamps - 1);
 }
@@ -384,6 +392,7 @@ hipError_t launch_persistent(const PersistentLaunch &p, int32_t grid, hipStream_
   a.hq = p.hq;
   a.sh = p.sh;
   a.y = p.y;
+  a.y16 = p.y16;
   a.out = p.out;
   a.bar = p.bar;
   a.block_m = p.block_m;

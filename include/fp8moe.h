@@ -240,7 +240,10 @@ size_t moe_workspace_bytes(const moe_dims *dims /*host*/);
 
 /* Forward pass of one W8A8 FP8 MoE layer: quantise x, router logits (or
  * logits_override), top-k + weights, permutation, gate/up + SiLU*up,
- * requantisation, down projection, weighted combine.
+ * requantisation, down projection, weighted combine.  Intermediates stay in
+ * the workspace: h in fp32, hq in e4m3, and the down projection's outputs y
+ * in fp16 on their way to the combine (values beyond +-65504 saturate; with
+ * MOE_F_NO_REQUANT, h and y stay fp32).
  * x [T][d] fp32; w_router [E][d] (may be NULL when logits_override is given);
  * router_bias [E] or NULL; k_per_token [T] or NULL (all k_max);
  * logits_override [T][E] or NULL; out [T][d] fp32;

@@ -122,18 +122,27 @@ def test_weights_match_oracle_quantiser(small):
     np.testing.assert_array_equal(to_np(small.dw.s_down), small.qw.s_down)
 
 
-def test_deterministic_and_batch_invariant(small):
+@pytest.mark.parametrize("splits", [None, 1])
+def test_deterministic_and_batch_invariant(small, splits, monkeypatch):
+    """Repeated forwards are identical; a token's output does not depend on
+    its batch (the ELDR page: outputs identical to standard top-k when only
+    placement changes).  With one K split of the down projection (pinned) the
+    batches differ only in rounding order, within 1e-6.  Left to the planner,
+    the two batch sizes may take different split counts, and the fp16 y
+    slabs then round different partial sums: each element within a few fp16
+    half-ulps (2^-11 relative each), 2e-3 over the rows."""
+    if splits is not None:
+        monkeypatch.setenv("FP8MOE_DOWN_SPLITS", str(splits))
     layer = small.layer()
     kpt = small.kpt
     a = layer.forward(small.x, k_per_token=kpt)
     b = layer.forward(small.x, k_per_token=kpt)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    # a token's output does not depend on its batch (same kernels, same routing)
     sub = torch.tensor([0, small.spec.T - 1], device=dev())
     c = layer.forward(small.x[sub].contiguous(), k_per_token=None if kpt is None else kpt[sub].contiguous())
     torch.cuda.synchronize()
-    assert rel_l2(to_np(c), to_np(a)[to_np(sub)]) < 1e-6
+    assert rel_l2(to_np(c), to_np(a)[to_np(sub)]) < (1e-6 if splits == 1 else 2e-3)
 
 
 def _persistent_vs_staged(L: Layer, T=None, no_requant=False, bias=None):
