@@ -277,7 +277,33 @@ struct Layout {
   int32_t capacity, rows_total, max_items, row_chunk, msub, msub_big, splits;
   bool nt_gu, nt_dn;  // non-temporal weight loads
   GemmPlan gu, dn;
+  bool ares_gu, ares_dn;     // A-resident tiles (short K)
+  int32_t ntg_gu, ntg_dn;    // their N-tiles per workgroup
 };
+
+// A-resident tiles for a short-K GEMM: the items' whole K range in LDS
+// (ares_fits), two-operand plans of up to 128-row items, outside the single
+// persistent launch.  FP8MOE_ARES=0 keeps the per-tile kernels (tile tuning).
+bool use_ares(const moe_dims *d, const GemmPlan &p, int32_t msub_big, bool gate_up) {
+  static const int env = env_int("FP8MOE_ARES", 1);
+  if (!env || (d->flags & MOE_F_PERSISTENT) || p.nb != 2 || msub_big > 8) return false;
+  if (!gate_up && (d->flags & MOE_F_NO_REQUANT)) return false;
+  return ares_fits(msub_big, gate_up ? d->d : d->f);
+}
+
+// N-tiles per A-resident workgroup: about two workgroups per slot in all.
+int32_t ares_ntg(const moe_dims *d, const GemmPlan &p, int32_t msub_big, bool gate_up) {
+  const int N = gate_up ? d->f : d->d;
+  const int ch_wg = (p.waves + 1) * (gate_up ? 16 : 32);
+  const int n_tiles = (N + ch_wg - 1) / ch_wg;
+  const double units = expected_items(d, msub_big) * n_tiles;
+  const double slots = (double)device_cus() * ((p.waves + 1) <= 6 ? 2 : 1);
+  const int forced = env_int("FP8MOE_ARES_NTG", 0);  // tile-tuning override
+  int ntg = forced > 0 ? forced : (int)(units / (2.0 * slots));
+  // the workgroup's weight scales are staged in LDS (32 floats per wave and tile)
+  ntg = std::min(ntg, kAresScaleFloats / ((p.waves + 1) * 32));
+  return std::max(1, std::min(ntg, n_tiles));
+}
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -292,7 +318,12 @@ Layout layout_of(const moe_dims *d) {
   // the single launch runs one row-pass shape: items cut at 16*msub rows
   L.msub_big = (L.gu.nb == 2 && L.dn.nb == 2 && !persistent) ? choose_msub_big(d, L.msub) : L.msub;
   L.row_chunk = 16 * L.msub_big;
-  L.splits = L.dn.splits;
+  // A-resident tiles where a workgroup gets at least two tiles of short K
+  L.ntg_gu = ares_ntg(d, L.gu, L.msub_big, true);
+  L.ntg_dn = ares_ntg(d, L.dn, L.msub_big, false);
+  L.ares_gu = use_ares(d, L.gu, L.msub_big, true) && L.ntg_gu >= 2;
+  L.ares_dn = use_ares(d, L.dn, L.msub_big, false) && L.ntg_dn >= 2;
+  L.splits = L.ares_dn ? 1 : L.dn.splits;
   {
     int32_t sp, ks;
     down_split_geometry(d->f, L.msub, L.splits, &sp, &ks);
@@ -484,14 +515,27 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   rs.max_items = L.max_items;
   const ExpertWeights ew = to_internal(w);
   mark(3);
-  if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, L.nt_gu, st), "gate_up"))) return s;
+  if (L.ares_gu) {
+    if ((s = hip_status(launch_ares(rs, xq, sx, ew, h, nullptr, true, L.msub_big, L.gu.waves + 1,
+                                    L.ntg_gu, L.nt_gu, st),
+                        "gate_up")))
+      return s;
+  } else if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, L.nt_gu, st), "gate_up"))) {
+    return s;
+  }
   mark(4);
   if (requant) {
     if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
-    if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, nullptr, y16, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
-                        "down")))
+    if (L.ares_dn) {
+      if ((s = hip_status(launch_ares(rs, hq, sh, ew, nullptr, y16, false, L.msub_big,
+                                      L.dn.waves + 1, L.ntg_dn, L.nt_dn, st),
+                          "down")))
+        return s;
+    } else if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, nullptr, y16, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),
+                               "down"))) {
       return s;
+    }
   } else {
     mark(5);
     if ((s = hip_status(launch_down(rs, nullptr, nullptr, h, ew, y, nullptr, L.msub, L.msub, 1, L.dn.waves, L.dn.nb, false, st), "down")))

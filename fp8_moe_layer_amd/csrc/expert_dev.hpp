@@ -55,6 +55,8 @@ struct GemmArgs {
   // Down projection: when set, y is written here in fp16 (same layout; values
   // beyond +-65504 saturate) instead of fp32 to `out`.
   _Float16 *out16 = nullptr;
+  // A-resident tiles (ares_tile): consecutive N-tiles per workgroup.
+  int32_t ntg = 1;
   // Decode down projection: tile t of expert e starts its K loop at step
   // ((t + 5e) * krot) % nks and wraps (0: no rotation).  When all of a
   // launch's workgroups run in one round they otherwise walk their weight
@@ -552,6 +554,202 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   }
 }
 
+
+// ------------------------------------------------------------------ A-resident grouped GEMM
+// Short K (the down projection of small experts, K = f = 192 .. 1408, and the
+// gate/up projection of decode batches with few rows per expert): the
+// item's activation rows for the WHOLE K range fit in LDS, so the workgroup
+// gathers them once and then walks g.ntg consecutive N-tiles of its item.
+// Every wave computes (no loader wave), the weight prefetch ring runs on
+// across tile boundaries (the next tile's first K steps are in flight during
+// the current tile's last steps and epilogue), and after the gather there is
+// no workgroup barrier: the A block is read-only.  The weight scales of all
+// the workgroup's channels are staged in LDS with the gather, so inside the
+// tile loop the only global loads are the weight stream (a load whose result
+// is needed early would make the in-order wait drain the prefetched weights).
+// The per-tile workgroups of wsgemm_tile pay a gather, a barrier chain and a
+// dependent start-up latency for every tile of two to sixteen K steps.
+//
+// LDS: A fragments [ksp][MSUB] of 2 KB (MFMA operand order, zero for rows
+// past the item and K past the end), the rows' activation scales, then the
+// channels' weight scales (gate and up interleaved for gate/up).
+constexpr int kAresLdsMax = 96 * 1024;
+__host__ __device__ constexpr int ares_lds_bytes(int msub, int ksp, int scale_floats) {
+  return msub * ksp * 2048 + 16 * msub * 4 + scale_floats * 4;
+}
+
+template <int NB, bool GATEUP>
+struct TilePtrs {
+  const uint8_t *bw[NB];
+  int ch[NB];
+  int nks;
+  // c0: the wave's first output channel (no memory access: addresses only)
+  __device__ __forceinline__ void set(const GemmArgs &g, bool shared, size_t ex, int c0, int nks_,
+                                      int lane) {
+    const int N = GATEUP ? g.rs.f : g.rs.d;
+    const int K = GATEUP ? g.rs.d : g.rs.f;
+    const int KT = (K + 127) >> 7;
+    nks = nks_;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int o;
+      const uint8_t *wbase;
+      if (GATEUP) {
+        o = c0 + (nb >> 1) * 16 + (lane & 15);
+        wbase = ((nb & 1) == 0 ? (shared ? g.w.ws_gate : g.w.w_gate) : (shared ? g.w.ws_up : g.w.w_up)) +
+                ex * (size_t)N * KT * 128;
+      } else {
+        o = c0 + nb * 16 + (lane & 15);
+        wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * KT * 128;
+      }
+      const int orow = o < N ? o : N - 1;
+      ch[nb] = o;
+      bw[nb] = wbase + (size_t)(orow >> 4) * KT * 2048 + lane * 16;
+    }
+  }
+  template <bool NT>
+  __device__ __forceinline__ void load(v8i (&b)[NB], int ks) const {
+    ks = ks < nks ? ks : nks - 1;
+    const int o0 = ks * 2048;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const v4i lo = NT ? load16_nt(bw[nb] + o0) : load16(bw[nb] + o0);
+      const v4i hi = NT ? load16_nt(bw[nb] + o0 + 1024) : load16(bw[nb] + o0 + 1024);
+      b[nb] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  }
+};
+
+template <int MSUB, bool GATEUP, bool NT, int PF>
+__device__ __forceinline__ void ares_tile(const GemmArgs &g, int bid, uint8_t *lds) {
+  constexpr int NB = 2;
+  constexpr int MP = 16 * MSUB;
+  constexpr int CH_WAVE = GATEUP ? 8 * NB : 16 * NB;
+  const RowSpace &rs = g.rs;
+  const int W = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));  // every wave computes
+  const int K = GATEUP ? rs.d : rs.f;
+  const int N = GATEUP ? rs.f : rs.d;
+  const int CH_WG = W * CH_WAVE;
+  const int n_tiles = (N + CH_WG - 1) / CH_WG;
+  const int n_groups = (n_tiles + g.ntg - 1) / g.ntg;
+  const int item_id = bid / n_groups;
+  const int t_begin = (bid - item_id * n_groups) * g.ntg;
+  const int t_end = min(n_tiles, t_begin + g.ntg);
+  int expert, row0, rows;
+  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  if (t_begin >= t_end) return;
+  const int nks = (K + 127) >> 7;
+  const int ksp = (nks + PF - 1) / PF * PF;  // K steps padded to the ring depth (zero A)
+  const bool shared = expert >= rs.E;
+  const size_t ex = (size_t)(shared ? expert - rs.E : expert);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15, kg = lane >> 4;
+  const int msub = (rows + 15) >> 4;
+  float *rsc = reinterpret_cast<float *>(lds + MSUB * ksp * 2048);
+  float *wsl = rsc + MP;  // weight scales of channels [t_begin * CH_WG, t_end * CH_WG)
+  const int c_first = t_begin * CH_WG;
+
+  // ---- the tiles' first weight steps, then the gather (piece q = (ks, m,
+  // half); wave w takes q = w, w + W, ...), the row and weight scales
+  TilePtrs<NB, GATEUP> cur, nxt;
+  cur.set(g, shared, ex, c_first + wave * CH_WAVE, nks, lane);
+  v8i ring[PF][NB];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) cur.template load<NT>(ring[s], s);
+  {
+    const uint8_t *arow[MSUB];
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m) {
+      const int r = m * 16 + ln;
+      const int grow = row0 + min(r, rows - 1);
+      const int sp = rs.sorted_pairs[min(grow, rs.capacity - 1)];
+      const int a = act_row<GATEUP>(rs, grow, sp, r < rows);
+      arow[m] = a < 0 ? nullptr : g.a + (size_t)a * K;
+    }
+    const int npieces = ksp * MSUB * 2;
+#pragma unroll 4
+    for (int q = wave; q < npieces; q += W) {
+      const int half = q & 1, m = (q >> 1) % MSUB, ks = (q >> 1) / MSUB;
+      const int kb = ks * 128 + half * 64 + kg * 16;
+      const uint8_t *base = arow[0];
+#pragma unroll
+      for (int mm = 1; mm < MSUB; ++mm)
+        if (mm == m) base = arow[mm];
+      const v4i v = (base && kb < K) ? load16(base + kb) : v4i{0, 0, 0, 0};
+      *reinterpret_cast<v4i *>(lds + (ks * MSUB + m) * 2048 + half * 1024 + lane * 16) = v;
+    }
+    for (int r = threadIdx.x; r < MP; r += blockDim.x) {
+      const int grow = row0 + min(r, rows - 1);
+      const int sp = rs.sorted_pairs[min(grow, rs.capacity - 1)];
+      const int a = act_row<GATEUP>(rs, grow, sp, r < rows);
+      rsc[r] = a < 0 ? 0.0f : g.a_scale[a];
+    }
+    const int nch = (t_end - t_begin) * CH_WG;
+    for (int i = threadIdx.x; i < nch; i += blockDim.x) {
+      const int o = min(c_first + i, N - 1);
+      if (GATEUP) {
+        wsl[2 * i] = (shared ? g.w.ss_gate : g.w.s_gate)[ex * N + o];
+        wsl[2 * i + 1] = (shared ? g.w.ss_up : g.w.s_up)[ex * N + o];
+      } else {
+        wsl[i] = (shared ? g.w.ss_down : g.w.s_down)[ex * N + o];
+      }
+    }
+  }
+  __syncthreads();
+
+  v4f acc[MSUB][NB];
+  const uint8_t *lds_lane = lds + lane * 16;
+  for (int t = t_begin; t < t_end; ++t) {
+    const bool has_next = t + 1 < t_end;
+    if (has_next) nxt.set(g, shared, ex, (t + 1) * CH_WG + wave * CH_WAVE, nks, lane);
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[m][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int ks0 = 0; ks0 < ksp; ks0 += PF) {
+#pragma unroll
+      for (int s = 0; s < PF; ++s) {
+        const int ks = ks0 + s;
+        const uint8_t *fa = lds_lane + ks * MSUB * 2048;
+        constexpr int MB = MSUB >= 4 ? 4 : MSUB;
+#pragma unroll
+        for (int mb = 0; mb < MSUB; mb += MB) {
+          if (mb < msub) {
+            v8i a[MB];
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+              const v4i a0 = *reinterpret_cast<const v4i *>(fa + (mb + j) * 2048);
+              const v4i a1 = *reinterpret_cast<const v4i *>(fa + (mb + j) * 2048 + 1024);
+              a[j] = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[mb + j][nb] = mfma_e4m3_16x16x128(a[j], ring[s][nb], acc[mb + j][nb]);
+          }
+        }
+        // step ks + PF: this tile's, else the next tile's first steps
+        if (ks + PF < ksp)
+          cur.template load<NT>(ring[s], ks + PF);
+        else if (has_next)
+          nxt.template load<NT>(ring[s], ks + PF - ksp);
+      }
+    }
+    // the epilogue's channels and their weight scales (from LDS)
+    WOperands<NB, GATEUP, NT> ep;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      ep.ch[nb] = cur.ch[nb];
+      const int i = min(cur.ch[nb], N - 1) - c_first;
+      ep.wsc[nb] = GATEUP ? wsl[2 * i + (nb & 1)] : wsl[i];
+    }
+    gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, ep, rsc, row0, 0, rows, msub, 0, lane);
+    if (has_next) cur = nxt;
+  }
+}
 
 // ------------------------------------------------------------------ prefill grouped GEMM
 // Row passes of 256 rows (prefill-sized batches re-read an expert's weights

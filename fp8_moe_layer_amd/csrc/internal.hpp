@@ -112,6 +112,23 @@ hipError_t launch_down(const RowSpace &rs, const uint8_t *hq, const float *sh, c
                        int32_t msub_big, int32_t splits, int32_t waves, int32_t nb,
                        bool stream_weights, hipStream_t stream);
 int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
+// A-resident grouped GEMM (short K): the work items' activation rows for the
+// whole K range in LDS, gathered once per workgroup; each workgroup of
+// `waves` computing waves takes `ntg` consecutive N-tiles of its item; no K
+// splits.  Applies when ares_fits(msub, K) (msub = the items' row passes,
+// K <= kAresMaxK, the A block within the LDS budget); requires the work
+// list.  Measured: it wins where K is a few steps and a workgroup takes
+// several tiles (MoE-Prism-shaped down projection, K = 192: 131 -> 115 us);
+// with K of 768 .. 2048 and one or two tiles per workgroup the per-tile
+// kernels stay faster (the larger gather and LDS footprint cost more than
+// the start-up latencies they save).
+constexpr int kAresMaxK = 512;
+constexpr int kAresScaleFloats = 4096;  // weight scales staged per workgroup: ntg * waves * 32 at most
+bool ares_fits(int32_t msub, int32_t K);
+hipError_t launch_ares(const RowSpace &rs, const uint8_t *a, const float *a_scale,
+                       const ExpertWeights &w, float *out, _Float16 *out16, bool gate_up,
+                       int32_t msub, int32_t waves, int32_t ntg, bool stream_weights,
+                       hipStream_t stream);
 // Final K-split count and bytes per split for a requested split count.
 void down_split_geometry(int32_t f, int32_t msub, int32_t requested, int32_t *splits,
                          int32_t *ksplit);

@@ -100,6 +100,70 @@ __global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
     wsgemm_tile<ML, 2, GATEUP, NT>(g, blockIdx.x, abuf);
 }
 
+// A-resident tiles (ares_tile): every wave computes; LDS sized at launch.
+template <int MSUB>
+constexpr int ares_pf() { return MSUB >= 8 ? 2 : 4; }
+
+template <int MSUB, bool GATEUP, bool NT>
+__global__ __launch_bounds__(kGemmMaxThreads) void ares_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t ares_lds[];
+  ares_tile<MSUB, GATEUP, NT, ares_pf<MSUB>()>(g, blockIdx.x, ares_lds);
+}
+
+template <bool GATEUP, bool NT>
+static hipError_t launch_ares_t(const GemmArgs &g, int msub, int waves, hipStream_t stream) {
+  const int N = GATEUP ? g.rs.f : g.rs.d;
+  const int K = GATEUP ? g.rs.d : g.rs.f;
+  const int ch_wg = waves * (GATEUP ? 16 : 32);
+  const int n_tiles = (N + ch_wg - 1) / ch_wg;
+  const int blocks = g.rs.max_items * ((n_tiles + g.ntg - 1) / g.ntg);
+  if (blocks == 0) return hipSuccess;
+  const int nks = (K + 127) / 128;
+  const int scales = g.ntg * ch_wg * (GATEUP ? 2 : 1);
+  auto go = [&](auto kern, int ms, int pf) {
+    const int ksp = (nks + pf - 1) / pf * pf;
+    kern<<<blocks, waves * 64, ares_lds_bytes(ms, ksp, scales), stream>>>(g);
+    return hipGetLastError();
+  };
+  switch (msub) {
+    case 1: return go(ares_kernel<1, GATEUP, NT>, 1, ares_pf<1>());
+    case 2: return go(ares_kernel<2, GATEUP, NT>, 2, ares_pf<2>());
+    case 4: return go(ares_kernel<4, GATEUP, NT>, 4, ares_pf<4>());
+    case 8: return go(ares_kernel<8, GATEUP, NT>, 8, ares_pf<8>());
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// LDS of the A block and row scales (the weight scales come on top, at most
+// kAresScaleFloats of them).
+static int32_t ares_lds_need(int32_t msub, int32_t K) {
+  if (msub != 1 && msub != 2 && msub != 4 && msub != 8) return 1 << 30;
+  const int pf = msub >= 8 ? 2 : 4;
+  const int nks = (K + 127) / 128;
+  return ares_lds_bytes(msub, (nks + pf - 1) / pf * pf, 0);
+}
+
+bool ares_fits(int32_t msub, int32_t K) {
+  return K <= kAresMaxK && ares_lds_need(msub, K) + kAresScaleFloats * 4 <= kAresLdsMax;
+}
+
+hipError_t launch_ares(const RowSpace &rs, const uint8_t *a, const float *a_scale,
+                       const ExpertWeights &w, float *out, _Float16 *out16, bool gate_up,
+                       int32_t msub, int32_t waves, int32_t ntg, bool stream_weights,
+                       hipStream_t stream) {
+  if (!rs.items || !ares_fits(msub, gate_up ? rs.d : rs.f) || waves < 1 || waves > kGemmMaxWaves + 1 ||
+      ntg < 1 || ntg * waves * (gate_up ? 32 : 32) > kAresScaleFloats)
+    return hipErrorInvalidValue;
+  GemmArgs g{rs, a, a_scale, nullptr, w, out, 1, gate_up ? rs.d : rs.f};
+  g.out16 = out16;
+  g.ntg = ntg;
+  if (gate_up)
+    return stream_weights ? launch_ares_t<true, true>(g, msub, waves, stream)
+                          : launch_ares_t<true, false>(g, msub, waves, stream);
+  return stream_weights ? launch_ares_t<false, true>(g, msub, waves, stream)
+                        : launch_ares_t<false, false>(g, msub, waves, stream);
+}
+
 __global__ __launch_bounds__(256) void down_f32_kernel(GemmArgs g) {
   down_f32_tile(g, blockIdx.x, threadIdx.x);
 }

@@ -239,6 +239,27 @@ def test_streamed_weight_loads(small, nt, monkeypatch):
     _check(small, no_requant=True)
 
 
+ARES_SPECS = {
+    "ares-shared": wl.TINY.with_(T=40, d=1024, f=192, E=16, k=4, n_shared=1),
+    "ares-tail": wl.TINY.with_(T=200, d=640, f=448, E=32, k=6, k_choices=(2, 4, 6)),
+}
+
+
+@pytest.mark.parametrize("name", list(ARES_SPECS))
+@pytest.mark.parametrize("ntg", [2, 3, 8])
+def test_a_resident_down_tiles(name, ntg, monkeypatch):
+    """The down projection on A-resident tiles (the item's rows for the whole
+    K range in LDS, several N-tiles per workgroup, weights prefetched across
+    tile boundaries), forced onto small layers with a partial last tile, a
+    64-byte K tail and shared experts: every token within the bar."""
+    monkeypatch.setenv("FP8MOE_ARES_NTG", str(ntg))
+    L = Layer(ARES_SPECS[name])
+    err, worst = _check(L)
+    for T in (1, 7):
+        _check(L, T=T)
+    print(f"{name} ntg={ntg} rel-L2 {err:.3e} worst token {worst:.3e}")
+
+
 # ----------------------------------------------------------------- full-size layers, every token
 
 def test_mixtral_decode_sweep():
