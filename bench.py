@@ -78,6 +78,8 @@ def parse(argv=None):
     p.add_argument("--parity-tokens", type=int, default=64,
                    help="tokens of each point compared with the oracle")
     p.add_argument("--no-requant", action="store_true")
+    p.add_argument("--no-persistent", action="store_true",
+                   help="skip timing the single persistent launch (profiling runs)")
     p.add_argument("--group", action="store_true",
                    help="qwen3: decode batches of 64 from a pool of 512 tokens, in arrival order "
                         "and grouped by expert affinity (moe_group_tokens)")
@@ -384,7 +386,7 @@ def time_persistent(torch, shape, T, bias, x, kpt, steps, warmup, sh):
             "status": status, "phase_ends_us": lays[0].persistent_stamps()}
 
 
-def measure_point(torch, fp8, shape, T, bias, steps, warmup, sh, parity_n, label):
+def measure_point(torch, fp8, shape, T, bias, steps, warmup, sh, parity_n, label, persistent=True):
     """Time one layer shape at batch T; roofline fractions of the layer."""
     spec = shape.spec
     layers = shape.layers(T, bias)
@@ -416,13 +418,14 @@ def measure_point(torch, fp8, shape, T, bias, steps, warmup, sh, parity_n, label
         t = stages["down"] * 1e-6
         pt["down"] = {"us": stages["down"], "hbm_frac": round(acc["down_bytes"] / t / PEAK_HBM, 4),
                       "mfma_frac": round(acc["down_flops"] / t / PEAK_FP8, 4)}
-    pt["persistent"] = time_persistent(torch, shape, T, bias, x, kpt, steps, warmup, sh)
+    if persistent:
+        pt["persistent"] = time_persistent(torch, shape, T, bias, x, kpt, steps, warmup, sh)
     if parity_n:
         bias_np = None if bias is None else bias.cpu().numpy()
         pt["parity"] = parity_sample(shape, T, x, kpt, bias_np, out, ids, parity_n)
     log(f"{label}: {pt['us_mean']} us (median {pt['us_median']}), D={acc['distinct_experts']}, "
         f"hbm {pt['hbm_frac']}, mfma {pt['mfma_frac']}, stages {stages}, "
-        f"persistent {pt['persistent']}, parity {pt.get('parity')}")
+        f"persistent {pt.get('persistent')}, parity {pt.get('parity')}")
     del layers
     return pt, ms, dist, stages, acc, out, ids
 
@@ -591,7 +594,7 @@ def main():
 
     # ---- the same steps as one persistent cooperative launch each
     persistent = None
-    if not args.no_requant:
+    if not args.no_requant and not args.no_persistent:
         persistent = time_persistent(torch, shape, T, bias, x, kpt, args.steps, args.warmup, sh)
         persistent["staged_us_mean"] = round(ms * 1e3, 2)
         log(f"persistent single launch: {persistent}")
