@@ -291,17 +291,21 @@ bool use_ares(const moe_dims *d, const GemmPlan &p, int32_t msub_big, bool gate_
   return ares_fits(msub_big, gate_up ? d->d : d->f);
 }
 
+// Waves of an A-resident workgroup: the plan's waves plus the loader's slot
+// (every wave computes), at most kAresMaxWaves.
+int32_t ares_waves(const GemmPlan &p) { return std::min(p.waves + 1, kAresMaxWaves); }
+
 // N-tiles per A-resident workgroup: about two workgroups per slot in all.
 int32_t ares_ntg(const moe_dims *d, const GemmPlan &p, int32_t msub_big, bool gate_up) {
   const int N = gate_up ? d->f : d->d;
-  const int ch_wg = (p.waves + 1) * (gate_up ? 16 : 32);
+  const int ch_wg = ares_waves(p) * (gate_up ? 16 : 32);
   const int n_tiles = (N + ch_wg - 1) / ch_wg;
   const double units = expected_items(d, msub_big) * n_tiles;
-  const double slots = (double)device_cus() * ((p.waves + 1) <= 6 ? 2 : 1);
+  const double slots = (double)device_cus() * (ares_waves(p) <= 6 ? 2 : 1);
   const int forced = env_int("FP8MOE_ARES_NTG", 0);  // tile-tuning override
   int ntg = forced > 0 ? forced : (int)(units / (2.0 * slots));
   // the workgroup's weight scales are staged in LDS (32 floats per wave and tile)
-  ntg = std::min(ntg, kAresScaleFloats / ((p.waves + 1) * 32));
+  ntg = std::min(ntg, kAresScaleFloats / (ares_waves(p) * 32));
   return std::max(1, std::min(ntg, n_tiles));
 }
 
@@ -516,7 +520,7 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   const ExpertWeights ew = to_internal(w);
   mark(3);
   if (L.ares_gu) {
-    if ((s = hip_status(launch_ares(rs, xq, sx, ew, h, nullptr, true, L.msub_big, L.gu.waves + 1,
+    if ((s = hip_status(launch_ares(rs, xq, sx, ew, h, nullptr, true, L.msub_big, ares_waves(L.gu),
                                     L.ntg_gu, L.nt_gu, st),
                         "gate_up")))
       return s;
@@ -529,7 +533,7 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
     mark(5);
     if (L.ares_dn) {
       if ((s = hip_status(launch_ares(rs, hq, sh, ew, nullptr, y16, false, L.msub_big,
-                                      L.dn.waves + 1, L.ntg_dn, L.nt_dn, st),
+                                      ares_waves(L.dn), L.ntg_dn, L.nt_dn, st),
                           "down")))
         return s;
     } else if ((s = hip_status(launch_down(rs, hq, sh, nullptr, ew, nullptr, y16, L.msub, L.msub_big, L.splits, L.dn.waves, L.dn.nb, L.nt_dn, st),

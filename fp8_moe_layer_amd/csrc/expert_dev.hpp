@@ -202,7 +202,10 @@ __device__ __forceinline__ float exp_neg(float g) {
   return __builtin_amdgcn_exp2f(y) * (1.0f + r * kLn2);
 }
 
-template <int MSUB, int NB, bool GATEUP, bool NT>
+// O16 (down projection): 1 writes y in fp16 (g.out16), 0 in fp32 (g.out), -1
+// decides at run time by whether g.out16 is set (a kernel that knows which
+// lets the compiler drop the other path's registers).
+template <int MSUB, int NB, bool GATEUP, bool NT, int O16 = -1>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc)[MSUB][NB],
                                               const WOperands<NB, GATEUP, NT> &wo, const float *rsc,
                                               int row0, int p0, int prow, int msub, int split,
@@ -218,6 +221,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
   // output stream does not push the weight stream's neighbours (activation
   // rows, tables) out of L2.
   const bool full = prow == 16 * MSUB;
+  const bool to16 = O16 == 1 || (O16 < 0 && g.out16 != nullptr);
   if (GATEUP) {
 #pragma unroll
     for (int cg = 0; cg < NB / 2; ++cg) {
@@ -258,7 +262,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
     }
   } else {
     const size_t yoff = (size_t)split * (rs.capacity + rs.S * rs.T) * N + (size_t)(row0 + p0 + kg * 4) * N;
-    if (g.out16) {
+    if (to16) {
       // fp16 y: lanes ln and ln^1 hold channels c, c+1 of a row; the even lane
       // stores both as one 32-bit word (the odd lane's value comes over DPP,
       // in every lane before any store condition).  A wave covers 64 bytes of
@@ -776,7 +780,7 @@ struct PfChunk {
   static constexpr int LDS = 2 * BYTES + 2 * MP * (int)sizeof(float);  // + scale table per pass parity
 };
 
-template <bool GATEUP>
+template <bool GATEUP, int O16 = -1>
 __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *abuf) {
   using C = PfChunk;
   constexpr int MSUB = C::MSUB, NB = 2, NW = kPfWaves;
@@ -909,7 +913,7 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *abu
         barrier_lds();
       }
     }
-    gemm_epilogue<MSUB, NB, GATEUP, false>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
+    gemm_epilogue<MSUB, NB, GATEUP, false, O16>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
   }
 }
 

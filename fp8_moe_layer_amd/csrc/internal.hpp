@@ -123,6 +123,7 @@ int32_t down_splits_used(int32_t f, int32_t msub, int32_t splits);
 // kernels stay faster (the larger gather and LDS footprint cost more than
 // the start-up latencies they save).
 constexpr int kAresMaxK = 512;
+constexpr int kAresMaxWaves = 8;       // waves per A-resident workgroup (all compute)
 constexpr int kAresScaleFloats = 4096;  // weight scales staged per workgroup: ntg * waves * 32 at most
 bool ares_fits(int32_t msub, int32_t K);
 hipError_t launch_ares(const RowSpace &rs, const uint8_t *a, const float *a_scale,

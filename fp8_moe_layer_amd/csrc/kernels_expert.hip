@@ -59,7 +59,7 @@ __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMax
 // channel tiles of the same items (same activation rows) and the passes of
 // the same expert (same weight tiles) side by side.  Measured at a
 // 65536-row batch: L2 misses of the gate/up GEMM 2.4 GB -> 1.0 GB.
-template <bool GATEUP>
+template <bool GATEUP, int O16>
 __global__ __launch_bounds__(kPfWaves * 64) void pfgemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t abuf[PfChunk::LDS];
   int bid = blockIdx.x;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void pfgemm_kernel(GemmArgs g) {
       bid = x * q + min(x, r) + j;  // XCD x: blocks [x*q + min(x, r), +q + (x < r))
     }
   }
-  pf_tile<GATEUP>(g, bid, abuf);
+  pf_tile<GATEUP, O16>(g, bid, abuf);
 }
 
 // Two row-pass shapes in one launch.  Work items are cut at 16*ML rows; an
@@ -104,8 +104,10 @@ __global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
 template <int MSUB>
 constexpr int ares_pf() { return MSUB >= 8 ? 2 : 4; }
 
+// At most eight waves (two per SIMD, up to 256 VGPRs each: the eight-row-group
+// tiles need more than the 168 of nine waves).
 template <int MSUB, bool GATEUP, bool NT>
-__global__ __launch_bounds__(kGemmMaxThreads) void ares_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kAresMaxWaves * 64) void ares_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t ares_lds[];
   ares_tile<MSUB, GATEUP, NT, ares_pf<MSUB>()>(g, blockIdx.x, ares_lds);
 }
@@ -151,7 +153,7 @@ hipError_t launch_ares(const RowSpace &rs, const uint8_t *a, const float *a_scal
                        const ExpertWeights &w, float *out, _Float16 *out16, bool gate_up,
                        int32_t msub, int32_t waves, int32_t ntg, bool stream_weights,
                        hipStream_t stream) {
-  if (!rs.items || !ares_fits(msub, gate_up ? rs.d : rs.f) || waves < 1 || waves > kGemmMaxWaves + 1 ||
+  if (!rs.items || !ares_fits(msub, gate_up ? rs.d : rs.f) || waves < 1 || waves > kAresMaxWaves ||
       ntg < 1 || ntg * waves * (gate_up ? 32 : 32) > kAresScaleFloats)
     return hipErrorInvalidValue;
   GemmArgs g{rs, a, a_scale, nullptr, w, out, 1, gate_up ? rs.d : rs.f};
@@ -240,7 +242,10 @@ static hipError_t launch_pf(const GemmArgs &g, hipStream_t stream) {
   const int n_tiles = (N + ch_wg - 1) / ch_wg;
   const int blocks = grid_items(g.rs) * n_tiles * g.splits;
   if (blocks == 0) return hipSuccess;
-  pfgemm_kernel<GATEUP><<<blocks, kPfWaves * 64, 0, stream>>>(g);
+  if (g.out16)
+    pfgemm_kernel<GATEUP, 1><<<blocks, kPfWaves * 64, 0, stream>>>(g);
+  else
+    pfgemm_kernel<GATEUP, 0><<<blocks, kPfWaves * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 

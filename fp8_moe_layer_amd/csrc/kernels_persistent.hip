@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kPThreads) void moe_persistent_kernel(PersistArgs a
     if constexpr (PF) {
       const int n = rs.max_items * ((d + kPfWaves * 32 - 1) / (kPfWaves * 32)) * a.splits;
       for (int b = B; b < n; b += G) {
-        pf_tile<false>(g, b, lds);
+        pf_tile<false, 1>(g, b, lds);  // the requantised path keeps y in fp16
         __syncthreads();
       }
     } else {
