@@ -17,6 +17,7 @@ import torch
 
 _HERE = pathlib.Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libfp8moe.so"
+DEBUG_LIB_PATH = _HERE / "libfp8moe_debug.so"  # device-checked build of the same sources
 
 MOE_F_NO_REQUANT = 1
 MOE_F_PERSISTENT = 2
@@ -332,6 +333,77 @@ def combine(dm: Dims, perm: dict, y, topk_ids, topk_w, stream=None):
 
 def workspace_bytes(dm: Dims) -> int:
     return int(_workspace_bytes(C.byref(dm)))
+
+
+class DebugLibrary:
+    """The device-checked build of the same sources (libfp8moe_debug.so,
+    compiled with FP8MOE_DEBUG): kernels check the layer's preconditions
+    (k_per_token in [1, k_max], finite logits and activations, top-k ids in
+    [-1, E)) and the permutation's index invariants; every call that enqueues
+    work waits for it and returns MOE_ERR_DEVICE_CHECK (7) naming the failed
+    checks.  It synchronises, so it is for testing, not for timing or graph
+    capture.  Calls return (status, error text) instead of raising."""
+
+    def __init__(self):
+        if not DEBUG_LIB_PATH.exists():
+            raise ImportError(f"{DEBUG_LIB_PATH} is not built (fp8_moe_layer_amd/build.py --debug)")
+        lib = C.CDLL(str(DEBUG_LIB_PATH))
+
+        def sig(name, restype, *argtypes):
+            fn = getattr(lib, name)
+            fn.restype = restype
+            fn.argtypes = list(argtypes)
+            return fn
+
+        self._fwd = sig("moe_fused_forward", _i32, _DP, _vp, _vp, _vp, _vp, _WP, _vp, _vp, _vp,
+                        _vp, _vp, C.c_size_t, _vp)
+        self._topk = sig("moe_route_topk", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
+        self._permute = sig("moe_permute", _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                            _vp, _vp, _vp, _vp)
+        self.workspace_bytes = sig("moe_workspace_bytes", C.c_size_t, _DP)
+        self.status_str = sig("moe_status_str", C.c_char_p, _i32)
+        self._last_error = sig("moe_last_error", C.c_char_p)
+        self.checks = int(sig("moe_debug_checks", _i32)())
+
+    def _result(self, rc: int):
+        return int(rc), (self._last_error() or b"").decode()
+
+    def forward(self, layer: "MoELayer", x: torch.Tensor, k_per_token=None, logits_override=None,
+                out=None, topk_ids=None, stream=None):
+        """layer's forward through the debug build: (status, text, out)."""
+        T = x.shape[0]
+        dm = layer.dims(T)
+        if out is None:
+            out = torch.empty((T, layer.w.d), dtype=torch.float32, device=x.device)
+        n = int(self.workspace_bytes(C.byref(dm)))
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+        rc = self._fwd(C.byref(dm), _ptr(x, torch.float32), _ptr(layer.w_router, torch.float32),
+                       _ptr(layer.router_bias, torch.float32), _ptr(k_per_token, torch.int32),
+                       C.byref(layer._wstruct), _ptr(logits_override, torch.float32), _ptr(out),
+                       _ptr(topk_ids, torch.int32), None, _ptr(ws), n, _stream(stream))
+        return (*self._result(rc), out)
+
+    def route_topk(self, logits: torch.Tensor, k_max: int, k_per_token=None, stream=None):
+        """(status, text, ids, w) of moe_route_topk through the debug build."""
+        T, E = logits.shape
+        ids = torch.empty((T, k_max), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, k_max), dtype=torch.float32, device=logits.device)
+        rc = self._topk(_ptr(logits, torch.float32), T, E, k_max, _ptr(k_per_token, torch.int32),
+                        _ptr(ids), _ptr(w), _stream(stream))
+        return (*self._result(rc), ids, w)
+
+    def permute(self, topk_ids: torch.Tensor, E: int, block_m: int = 16, stream=None):
+        """(status, text) of moe_permute through the debug build."""
+        T, k = topk_ids.shape
+        cap = capacity(T, E, k, block_m)
+        dv = topk_ids.device
+        i32 = dict(dtype=torch.int32, device=dv)
+        sp, off = torch.empty(cap, **i32), torch.empty(E + 1, **i32)
+        be = torch.empty((cap + block_m - 1) // block_m, **i32)
+        inv, nb = torch.empty(T * k, **i32), torch.empty(1, **i32)
+        rc = self._permute(_ptr(topk_ids, torch.int32), T, E, k, block_m, cap, _ptr(sp), _ptr(off),
+                           _ptr(be), _ptr(inv), _ptr(nb), _stream(stream))
+        return self._result(rc)
 
 
 class MoELayer:

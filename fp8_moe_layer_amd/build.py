@@ -1,7 +1,9 @@
 """Build the gfx950 HIP library libfp8moe.so in-tree with hipcc.
 
 The library is the whole compute path of the layer; the Python package only
-marshals arguments to its C ABI (include/fp8moe.h).
+marshals arguments to its C ABI (include/fp8moe.h).  `debug=True` builds the
+same sources with FP8MOE_DEBUG into libfp8moe_debug.so: device-side checks of
+the preconditions and index invariants, reported by every entry point.
 """
 from __future__ import annotations
 
@@ -13,6 +15,7 @@ import sys
 HERE = pathlib.Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
 LIB = HERE / "libfp8moe.so"
+LIB_DEBUG = HERE / "libfp8moe_debug.so"
 SOURCES = ["kernels_route.hip", "kernels_permute.hip", "kernels_expert.hip", "kernels_persistent.hip",
            "abi.hip", "batching.hip"]
 ARCH = os.environ.get("FP8MOE_ARCH", "gfx950")
@@ -40,15 +43,19 @@ def _run(cmd, verbose):
     return res.returncode, err
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> pathlib.Path:
-    """Compile every HIP source into libfp8moe.so (always recompiles; the
-    sources compile in parallel, then link)."""
+def build(verbose: bool = False, resource_usage: bool = False, debug: bool = False) -> pathlib.Path:
+    """Compile every HIP source into libfp8moe.so, or with `debug` into
+    libfp8moe_debug.so (always recompiles; the sources compile in parallel,
+    then link)."""
     from concurrent.futures import ThreadPoolExecutor
 
-    objdir = HERE / "_build"
+    lib = LIB_DEBUG if debug else LIB
+    objdir = HERE / ("_build_debug" if debug else "_build")
     objdir.mkdir(exist_ok=True)
-    tmp = LIB.with_name(LIB.name + ".tmp")
+    tmp = lib.with_name(lib.name + ".tmp")
     flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    if debug:
+        flags = ["-DFP8MOE_DEBUG=1"] + flags
     if resource_usage:
         flags = ["-Rpass-analysis=kernel-resource-usage"] + flags
     jobs = []
@@ -67,9 +74,9 @@ def build(verbose: bool = False, resource_usage: bool = False) -> pathlib.Path:
                    [str(o) for o, _ in jobs], verbose)
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{err}")
-    tmp.replace(LIB)
-    return LIB
+    tmp.replace(lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, resource_usage="--usage" in sys.argv))
+    print(build(verbose=True, resource_usage="--usage" in sys.argv, debug="--debug" in sys.argv))

@@ -51,6 +51,26 @@ moe_status ok_status() { return ok(); }
 
 namespace {
 
+// The end of an entry point that enqueued work: in the debug build, wait for
+// it and report the device checks that failed; in the release library only
+// the status.
+moe_status done(moe_status s, const char *fn) {
+  if (s) return s;
+#ifdef FP8MOE_DEBUG
+  const uint32_t b = debug_take_route() | debug_take_permute() | debug_take_expert() |
+                     debug_take_persistent();
+  if (b)
+    return fail(MOE_ERR_DEVICE_CHECK, "%s: device checks failed (0x%x):%s%s%s%s%s%s", fn, b,
+                (b & 1u) ? " k_per_token outside [1, k_max];" : "",
+                (b & 2u) ? " non-finite logit or activation row;" : "",
+                (b & 4u) ? " top-k id outside [-1, E);" : "",
+                (b & 8u) ? " work item outside its expert's rows;" : "",
+                (b & 16u) ? " row index outside the row space;" : "",
+                (b & 0x80000000u) ? " the check words could not be read;" : "");
+#endif
+  return ok();
+}
+
 moe_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return MOE_OK;
   return fail(MOE_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -600,6 +620,7 @@ const char *moe_status_str(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_DEVICE_CHECK: return "device check failed (debug build)";
     default: return "unknown status";
   }
 }
@@ -607,6 +628,14 @@ const char *moe_status_str(moe_status s) {
 const char *moe_last_error(void) { return g_err; }
 
 int32_t moe_abi_version(void) { return FP8MOE_ABI_VERSION; }
+
+int32_t moe_debug_checks(void) {
+#ifdef FP8MOE_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 int64_t moe_capacity(int32_t T, int32_t E, int32_t k_max, int32_t block_m) {
   return capacity_of(T, E, k_max, block_m);
@@ -622,7 +651,7 @@ moe_status moe_quantize_rows(const float *x, int32_t rows, int32_t cols, uint8_t
   if (!aligned(x, 16) || !aligned(q, 4) || !aligned(scale, 4))
     return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte and q 4-byte aligned", fn);
   moe_status s = hip_status(launch_quantize_rows(x, rows, cols, q, scale, as_stream(stream)), fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 int64_t moe_packed_weight_bytes(int32_t rows, int32_t cols) {
@@ -643,7 +672,7 @@ moe_status moe_pack_weights(const uint8_t *codes, int32_t rows, int32_t cols, ui
   const uintptr_t na = (uintptr_t)rows * cols, nb = (uintptr_t)moe_packed_weight_bytes(rows, cols);
   if (a < b + nb && b < a + na) return fail(MOE_ERR_SHAPE, "%s: codes and packed overlap", fn);
   moe_status s = hip_status(launch_pack_weights(codes, rows, cols, packed, as_stream(stream)), fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 moe_status moe_router_logits(const float *x, const float *w_router, const float *bias, int32_t T,
@@ -657,7 +686,7 @@ moe_status moe_router_logits(const float *x, const float *w_router, const float 
     return fail(MOE_ERR_ALIGN, "%s: x and w_router must be 16-byte aligned", fn);
   moe_status s =
       hip_status(launch_router(x, w_router, bias, T, d, E, logits, as_stream(stream)), fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
@@ -669,7 +698,7 @@ moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k_m
     return fail(MOE_ERR_SHAPE, "%s: T=%d E=%d k_max=%d", fn, T, E, k_max);
   moe_status s = hip_status(
       launch_topk(logits, T, E, k_max, k_per_token, topk_ids, topk_w, as_stream(stream)), fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
@@ -689,7 +718,7 @@ moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_
                                            expert_offsets, block_expert, inv_pairs, n_blocks,
                                            nullptr, nullptr, 0, 0, as_stream(stream)),
                             fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 
@@ -724,7 +753,7 @@ moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint
   s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub, mbig, gp.waves, gp.nb, nt,
                                 as_stream(stream)),
                  fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t *hq,
@@ -750,7 +779,7 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y, nullptr,
                              msub, mbig, 1, dp.waves, dp.nb, nt, as_stream(stream)),
                  fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 moe_status moe_combine(const moe_dims *dims, int32_t capacity, const float *y,
@@ -767,7 +796,7 @@ moe_status moe_combine(const moe_dims *dims, int32_t capacity, const float *y,
     return fail(MOE_ERR_SHAPE, "%s: capacity=%d too small", fn, capacity);
   RowSpace rs = row_space(dims, capacity, nullptr, nullptr);
   s = hip_status(launch_combine(rs, y, nullptr, 1, topk_ids, topk_w, inv_pairs, out, as_stream(stream)), fn);
-  return s ? s : ok();
+  return done(s, fn);
 }
 
 size_t moe_workspace_bytes(const moe_dims *dims) {
@@ -803,9 +832,10 @@ moe_status moe_fused_forward_timed(const moe_dims *dims, const float *x, const f
                 workspace ? workspace_bytes : (size_t)0, L.total);
   if (!aligned(workspace, 256))
     return fail(MOE_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-  return enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
-                         topk_ids_out, topk_w_out, static_cast<char *>(workspace), L,
-                         reinterpret_cast<hipEvent_t const *>(stage_events), as_stream(stream));
+  return done(enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
+                              topk_ids_out, topk_w_out, static_cast<char *>(workspace), L,
+                              reinterpret_cast<hipEvent_t const *>(stage_events), as_stream(stream)),
+              fn);
 }
 
 moe_status moe_fused_forward_noalloc(const moe_dims *dims, const float *x, const float *w_router,
@@ -824,9 +854,10 @@ moe_status moe_fused_forward_noalloc(const moe_dims *dims, const float *x, const
                 fn, L.total, kStaticScratchBytes);
   void *ws = nullptr;
   if ((s = scratch_of_current_device(&ws, fn))) return s;
-  return enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
-                         topk_ids_out, topk_w_out, static_cast<char *>(ws), L, nullptr,
-                         as_stream(stream));
+  return done(enqueue_forward(dims, x, w_router, router_bias, k_per_token, w, logits_override, out,
+                              topk_ids_out, topk_w_out, static_cast<char *>(ws), L, nullptr,
+                              as_stream(stream)),
+              fn);
 }
 
 }  // extern "C"

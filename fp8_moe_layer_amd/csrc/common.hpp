@@ -20,6 +20,64 @@ constexpr int kMaxK = 32;         // slots per token
 constexpr int kMaxFfn = 16384;  // longest h row the requantisation holds in registers
 constexpr float kE4m3Max = 448.0f;
 
+// ---------------------------------------------------------------- debug checks
+// Built with FP8MOE_DEBUG (libfp8moe_debug.so), the kernels test the layer's
+// preconditions and index invariants as they go.  A failed check sets its
+// bit in a device word of the kernel's translation unit (an atomic OR
+// through the vector memory path), and the failing value is replaced by a
+// safe one (a clamped k, a dropped id, a skipped row), so a failed check
+// never becomes an out-of-bounds access.  After each entry point the host
+// collects and clears the words (debug_take_*).  In the release library
+// dcheck() only returns its condition (the safe replacement still applies;
+// checks that cost more than a compare are compiled in only when debugging).
+enum : uint32_t {
+  kDbgKPerToken = 1u << 0,  // k_per_token[t] outside [1, k_max]
+  kDbgNonFinite = 1u << 1,  // a non-finite router logit, or a non-finite row to quantise
+  kDbgTopkId = 1u << 2,     // a top-k id outside [-1, E)
+  kDbgPermute = 1u << 3,    // a work item outside the expert row space
+  kDbgRow = 1u << 4,        // a sorted pair or combine row index outside its range
+};
+#ifdef FP8MOE_DEBUG
+constexpr bool kDebugChecks = true;
+static __device__ uint32_t g_debug_bits;  // one word per translation unit
+__device__ __forceinline__ bool dcheck(bool ok, uint32_t bit) {
+  if (!ok) atomicOr(&g_debug_bits, bit);
+  return ok;
+}
+// Host: this translation unit's word, then cleared (the device is synchronised first).
+#define FP8MOE_DEBUG_TAKE(NAME)                                                            \
+  uint32_t debug_take_##NAME() {                                                           \
+    uint32_t v = 0, z = 0;                                                                 \
+    if (hipDeviceSynchronize() != hipSuccess ||                                            \
+        hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_bits), sizeof v, 0,                     \
+                            hipMemcpyDeviceToHost) != hipSuccess)                          \
+      return 0x80000000u;                                                                  \
+    if (v && hipMemcpyToSymbol(HIP_SYMBOL(g_debug_bits), &z, sizeof z, 0,                  \
+                               hipMemcpyHostToDevice) != hipSuccess)                       \
+      return v | 0x80000000u;                                                              \
+    return v;                                                                              \
+  }
+#else
+constexpr bool kDebugChecks = false;
+__device__ __forceinline__ bool dcheck(bool ok, uint32_t) { return ok; }
+#define FP8MOE_DEBUG_TAKE(NAME) \
+  uint32_t debug_take_##NAME() { return 0; }
+#endif
+
+// k of token t: k_per_token[t], clamped to [1, k_max] (the debug build
+// records a value outside it), or k_max without a per-token array.
+__device__ __forceinline__ int token_k(const int32_t *kpt, int t, int k_max) {
+  if (!kpt) return k_max;
+  const int k = kpt[t];
+  return dcheck(k >= 1 && k <= k_max, kDbgKPerToken) ? k : (k < 1 ? 1 : k_max);
+}
+
+// A top-k id as the permutation reads it: an id outside [-1, E) is dropped
+// (-1; the debug build records it).
+__device__ __forceinline__ int checked_id(int e, int E) {
+  return dcheck(e >= -1 && e < E, kDbgTopkId) ? e : -1;
+}
+
 // ---------------------------------------------------------------- e4m3 codec
 // gfx950's v_cvt_pk_fp8_f32 converts to OCP E4M3FN with round-to-nearest-even.
 // Inputs are clamped to +-448 first, which is the saturating rule for every
@@ -114,6 +172,11 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+__device__ __forceinline__ bool finite4(v4f v) {
+  return __builtin_isfinite(v.x) && __builtin_isfinite(v.y) && __builtin_isfinite(v.z) &&
+         __builtin_isfinite(v.w);
+}
+
 // ---------------------------------------------------------------- row quantisation
 // One wave per row.  amax over the row, r = 448/amax and s = amax/448 as two
 // correctly rounded fp32 divisions, codes = e4m3(x * r).  The same IEEE
@@ -125,6 +188,7 @@ __device__ __forceinline__ void quantize_row_wave(const float *__restrict__ x, i
   for (int i = lane * 4; i < cols; i += kWave * 4) {
     v4f v = *reinterpret_cast<const v4f *>(x + i);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if constexpr (kDebugChecks) dcheck(finite4(v), kDbgNonFinite);
   }
   amax = wave_max(amax);
   float r = 1.0f, s = 1.0f;
@@ -153,6 +217,7 @@ __device__ __forceinline__ void quantize_row_block(const float *__restrict__ x, 
     const int i = (j * NT + (int)threadIdx.x) * 4;
     v[j] = i < cols ? *reinterpret_cast<const v4f *>(x + i) : v4f{0.f, 0.f, 0.f, 0.f};
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    if constexpr (kDebugChecks) dcheck(finite4(v[j]), kDbgNonFinite);
   }
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;

@@ -72,6 +72,15 @@ __device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, in
     expert = it.expert;
     row0 = it.row0;
     rows = it.rows;
+    // an item lies inside its expert's rows (routed: [0, capacity); shared
+    // expert s: [capacity + s*T, +T))
+    if constexpr (kDebugChecks) {
+      const bool in = expert >= 0 && expert < rs.E + rs.S && row0 >= 0 && rows >= 0 &&
+                      (expert < rs.E ? row0 + rows <= rs.capacity
+                                     : row0 >= rs.capacity + (expert - rs.E) * rs.T &&
+                                           row0 + rows <= rs.capacity + (expert - rs.E + 1) * rs.T);
+      if (!dcheck(in, kDbgPermute)) return false;
+    }
   } else {
     expert = item_id;
     if (expert < rs.E) {
@@ -93,7 +102,12 @@ __device__ __forceinline__ int row_token(const RowSpace &rs, int grow) {
 }
 
 __device__ __forceinline__ bool row_real(const RowSpace &rs, int grow) {
-  return grow >= rs.capacity || rs.sorted_pairs[grow] < rs.T * rs.k_max;
+  if (grow >= rs.capacity) return true;
+  const int sp = rs.sorted_pairs[grow];
+  // a pair index or the padding sentinel T*k_max (checked in the debug build)
+  if constexpr (kDebugChecks)
+    if (!dcheck(sp >= 0 && sp <= rs.T * rs.k_max, kDbgRow)) return false;
+  return sp < rs.T * rs.k_max;
 }
 
 // Activation row read for expert row `grow` of a GEMM (the token for gate/up,
@@ -103,7 +117,9 @@ __device__ __forceinline__ bool row_real(const RowSpace &rs, int grow) {
 template <bool GATEUP>
 __device__ __forceinline__ int act_row(const RowSpace &rs, int grow, int sp, bool ok) {
   const bool sh_row = grow >= rs.capacity;
-  const bool real = sh_row | (sp < rs.T * rs.k_max);
+  bool real = sh_row | (sp < rs.T * rs.k_max);
+  // sp: a pair index or the padding sentinel T*k_max (checked in the debug build)
+  if constexpr (kDebugChecks) real = real && (sh_row || dcheck(sp >= 0 && sp <= rs.T * rs.k_max, kDbgRow));
   int a = grow;
   if (GATEUP) a = sh_row ? (grow - rs.capacity) % rs.T : sp / rs.k_max;
   return (ok & real) ? a : -1;
@@ -1009,6 +1025,7 @@ __device__ __forceinline__ void requant_row_wave(const RowSpace &rs, const float
     const int i = (j * kWave + lane) * 4;
     v[j] = i < f ? *reinterpret_cast<const v4f *>(x + i) : v4f{0.f, 0.f, 0.f, 0.f};
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    if constexpr (kDebugChecks) dcheck(finite4(v[j]), kDbgNonFinite);
   }
   amax = wave_max(amax);
   float r = 1.0f, s = 1.0f;
@@ -1088,7 +1105,9 @@ __device__ __forceinline__ Cols<cols_per_load<Y>()> combine_groups(
         const int id = ids[p], r = inv[p];
         wt[u] = w[p];
         ok[u] = id >= 0;
-        row[u] = id >= 0 ? r : 0;
+        // a slot's row lies in [0, capacity) (checked in the debug build)
+        if constexpr (kDebugChecks) ok[u] = ok[u] && dcheck(r >= 0 && r < rs.capacity, kDbgRow);
+        row[u] = ok[u] ? r : 0;
       } else {  // a shared row (weight 1: 1 * x == x), or past the end
         wt[u] = 1.0f;
         ok[u] = j < J;

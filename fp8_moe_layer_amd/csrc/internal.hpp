@@ -102,6 +102,14 @@ hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx
 // Per-row e4m3 requantisation of h (real rows only): hq codes, sh = amax/448.
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream);
+
+// Debug build (FP8MOE_DEBUG): the device-check bits of each kernel file since
+// the last call, after synchronising the device (bit 31: the read failed);
+// always 0 in the release library.
+uint32_t debug_take_route();
+uint32_t debug_take_permute();
+uint32_t debug_take_expert();
+uint32_t debug_take_persistent();
 // Down projection from hq/sh, or (h32 != nullptr) straight from fp32 h with
 // fp32 products.  `splits` > 1 cuts K = f into that many ranges (fewer if f
 // is short) whose partial sums go to separate y slabs [split][rows][d]; the

@@ -386,4 +386,7 @@ hipError_t launch_combine(const RowSpace &rs, const float *y, const _Float16 *y1
   return hipGetLastError();
 }
 
+// Debug build: this file's device-check word (see common.hpp).
+FP8MOE_DEBUG_TAKE(expert)
+
 }  // namespace fp8moe

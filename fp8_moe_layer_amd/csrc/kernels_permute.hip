@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_count_kernel(
   const int w0 = min(b1, b0 + wave * per), w1 = min(b1, w0 + per);
   for (int e = lane; e < E; e += kWave) cnt[wave * E + e] = 0;  // this wave's row
   __builtin_amdgcn_wave_barrier();
-  slice_count(ids, w0, w1, expert_bits(E), cnt + wave * E, lane);
+  slice_count(ids, w0, w1, E, expert_bits(E), cnt + wave * E, lane);
   __syncthreads();
   for (int e = tid; e < E; e += kSliceWaves * kWave) {
     int c[kSliceWaves];
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_scatter_kernel(
   const int nbits = expert_bits(E);
   for (int e = lane; e < E; e += kWave) cnt[wave * E + e] = 0;  // this wave's row
   __builtin_amdgcn_wave_barrier();
-  slice_count(ids, w0, w1, nbits, cnt + wave * E, lane);
+  slice_count(ids, w0, w1, E, nbits, cnt + wave * E, lane);
   // the slice's bases are read (above) before its inv_pairs entries are written (scatter)
   __syncthreads();
   for (int e = tid; e < E; e += kSliceWaves * kWave) {
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_scatter_kernel(
     }
   }
   __syncthreads();
-  slice_scatter(ids, w0, w1, nbits, cnt + wave * E, sorted_pairs, inv_pairs, lane);
+  slice_scatter(ids, w0, w1, E, nbits, cnt + wave * E, sorted_pairs, inv_pairs, lane);
 }
 
 constexpr int kManySlices = 4;  // at least this many slices: the multi-workgroup path
@@ -181,5 +181,8 @@ hipError_t launch_permute(const int32_t *ids, int32_t T, int32_t E, int32_t k_ma
                                                  items, n_items, row_chunk, T, n_shared);
   return hipGetLastError();
 }
+
+// Debug build: this file's device-check word (see common.hpp).
+FP8MOE_DEBUG_TAKE(permute)
 
 }  // namespace fp8moe

@@ -407,4 +407,7 @@ hipError_t launch_persistent(const PersistentLaunch &p, int32_t grid, hipStream_
   return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kPThreads), params, 0, stream);
 }
 
+// Debug build: this file's device-check word (see common.hpp).
+FP8MOE_DEBUG_TAKE(persistent)
+
 }  // namespace fp8moe

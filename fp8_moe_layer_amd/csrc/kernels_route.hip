@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_token_kernel(
   }
   __syncthreads();
   if (wave == 0)
-    topk_row_wave(ls, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+    topk_row_wave(ls, E, k_max, token_k(kpt, t, k_max), ids + (size_t)t * k_max,
                   w + (size_t)t * k_max, lane);
 }
 
@@ -313,5 +313,8 @@ hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
   topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, k_max, k_per_token, ids, w);
   return hipGetLastError();
 }
+
+// Debug build: this file's device-check word (see common.hpp).
+FP8MOE_DEBUG_TAKE(route)
 
 }  // namespace fp8moe

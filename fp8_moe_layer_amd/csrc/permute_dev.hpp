@@ -42,7 +42,7 @@ __device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int nbit
 
 // Pass 1 over one wave's slice [b0, b1): adds each expert's count to my[e].
 __device__ __forceinline__ void slice_count(const int32_t *__restrict__ ids, int b0, int b1,
-                                            int nbits, int *my, int lane) {
+                                            int E, int nbits, int *my, int lane) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // the slice's ids are fetched kBatch steps at a time so the loads overlap
   for (int base = b0; base < b1; base += kWave * kBatch) {
@@ -50,7 +50,7 @@ __device__ __forceinline__ void slice_count(const int32_t *__restrict__ ids, int
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int p = base + u * kWave + lane;
-      ev[u] = p < b1 ? ids[p] : -1;
+      ev[u] = p < b1 ? checked_id(ids[p], E) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -67,7 +67,7 @@ __device__ __forceinline__ void slice_count(const int32_t *__restrict__ ids, int
 // Pass 2 over the same slice: pair p of expert e goes to row my[e] + (its
 // rank among the equal experts before it in the step); my[e] advances.
 __device__ __forceinline__ void slice_scatter(const int32_t *__restrict__ ids, int b0, int b1,
-                                              int nbits, int *my, int32_t *__restrict__ sorted_pairs,
+                                              int E, int nbits, int *my, int32_t *__restrict__ sorted_pairs,
                                               int32_t *__restrict__ inv_pairs, int lane) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = b0; base < b1; base += kWave * kBatch) {
@@ -75,7 +75,7 @@ __device__ __forceinline__ void slice_scatter(const int32_t *__restrict__ ids, i
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int p = base + u * kWave + lane;
-      ev[u] = p < b1 ? ids[p] : -1;
+      ev[u] = p < b1 ? checked_id(ids[p], E) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -222,7 +222,7 @@ __device__ __forceinline__ void permute_block(
   int *my = cnt + wave * E;
   for (int e = lane; e < E; e += kWave) my[e] = 0;  // only this wave uses its row until the barrier
   __builtin_amdgcn_wave_barrier();
-  slice_count(ids, b0, b1, nbits, my, lane);
+  slice_count(ids, b0, b1, E, nbits, my, lane);
   __syncthreads();
 
   // exclusive prefix over waves per expert (all NW counts read first); totals
@@ -245,7 +245,7 @@ __device__ __forceinline__ void permute_block(
   // pass 2: scatter (rows from segment start + wave base + running count)
   for (int e = lane; e < E; e += kWave) my[e] += off[e];
   __builtin_amdgcn_wave_barrier();
-  slice_scatter(ids, b0, b1, nbits, my, sorted_pairs, inv_pairs, lane);
+  slice_scatter(ids, b0, b1, E, nbits, my, sorted_pairs, inv_pairs, lane);
 }
 
 // ------------------------------------------------------------------ many workgroups

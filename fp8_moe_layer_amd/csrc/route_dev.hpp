@@ -214,6 +214,12 @@ __device__ __forceinline__ void topk_row_wave_n(const float *l, int E, int k_max
     const int e = lane + c * kWave;
     lv[c] = c * kWave < E ? l[e < E ? e : E - 1] : 0.0f;
   }
+  if constexpr (kDebugChecks) {
+    bool fin = true;
+#pragma unroll
+    for (int c = 0; c < NS; ++c) fin &= !(lane + c * kWave < E) || __builtin_isfinite(lv[c]);
+    dcheck(fin, kDbgNonFinite);
+  }
   uint32_t key[NS];
 #pragma unroll
   for (int c = 0; c < NS; ++c) key[c] = lane + c * kWave < E ? order_key(lv[c]) : 0u;
@@ -268,7 +274,7 @@ __device__ __forceinline__ void topk_token_wave(const float *__restrict__ logits
                                                 int32_t *__restrict__ ids, float *__restrict__ w,
                                                 int t, int lane) {
   (void)T;
-  topk_row_wave(logits + (size_t)t * E, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+  topk_row_wave(logits + (size_t)t * E, E, k_max, token_k(kpt, t, k_max), ids + (size_t)t * k_max,
                 w + (size_t)t * k_max, lane);
 }
 
@@ -441,7 +447,7 @@ __device__ __forceinline__ void route_tile_block(
     }
     if (lane == 0) sx[t] = m != 0.0f ? m / kE4m3Max : 1.0f;
     if (ids)  // all experts in this block (E <= EW)
-      topk_row_wave(ls + r * EW, E, k_max, kpt ? kpt[t] : k_max, ids + (size_t)t * k_max,
+      topk_row_wave(ls + r * EW, E, k_max, token_k(kpt, t, k_max), ids + (size_t)t * k_max,
                     w + (size_t)t * k_max, lane);
   }
 }

@@ -38,8 +38,16 @@
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failing call returns a non-zero moe_status, enqueues nothing, and
  *     moe_last_error() describes the failure (thread-local text).
- *   - Preconditions NOT checked on the device: inputs are finite, every
- *     k_per_token[t] is in [1, k_max], every topk_ids entry is -1 or in [0, E).
+ *   - Preconditions the release library does not report: inputs are finite,
+ *     every k_per_token[t] is in [1, k_max], every topk_ids entry is -1 or in
+ *     [0, E).  Out-of-range values stay memory-safe (a k is clamped to
+ *     [1, k_max], an id outside [-1, E) is dropped), but the results are then
+ *     undefined.  The debug build of the same sources, libfp8moe_debug.so
+ *     (FP8MOE_DEBUG; moe_debug_checks() returns 1), checks them on the
+ *     device together with the permutation's index invariants, waits for its
+ *     work at the end of every call that enqueues any, and returns
+ *     MOE_ERR_DEVICE_CHECK naming the checks that failed.  It synchronises,
+ *     so it is not for graph capture or timing.
  *   - Calls on one stream are ordered; calls on different streams that share
  *     output or workspace buffers race.
  */
@@ -53,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FP8MOE_ABI_VERSION 4
+#define FP8MOE_ABI_VERSION 5
 
 typedef int32_t moe_status;
 enum {
@@ -63,7 +71,8 @@ enum {
   MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   MOE_ERR_UNSUPPORTED = 4, /* a flag or configuration this build does not run */
   MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than moe_workspace_bytes */
-  MOE_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  MOE_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  MOE_ERR_DEVICE_CHECK = 7 /* debug build only: a device-side check failed */
 };
 
 enum {
@@ -343,6 +352,9 @@ moe_status moe_fused_forward_timed(const moe_dims *dims /*host*/, const float *x
 const char *moe_status_str(moe_status s);
 const char *moe_last_error(void); /* thread-local detail of this thread's last failing call */
 int32_t moe_abi_version(void);
+/* 1 in the debug build (device-side checks, see the conventions above), 0 in
+ * the release library. */
+int32_t moe_debug_checks(void);
 
 #ifdef __cplusplus
 }

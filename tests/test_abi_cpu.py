@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "fp8moe.h")
 
 fp8 = pytest.importorskip("fp8_moe_layer_amd", reason="libfp8moe.so not built")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE_CHECK = range(8)
 FAKE = 0x10000  # an aligned non-null address; never dereferenced (validation fails first)
 
 
@@ -23,16 +23,33 @@ def _declared():
     return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
 
 
-def test_every_declared_symbol_is_exported():
+@pytest.mark.parametrize("debug", [False, True])
+def test_every_declared_symbol_is_exported(debug):
     names = _declared()
     assert len(names) >= 13
-    lib = C.CDLL(str(fp8.LIB_PATH))
+    path = fp8.DEBUG_LIB_PATH if debug else fp8.LIB_PATH
+    if debug and not path.exists():
+        pytest.skip("libfp8moe_debug.so not built")
+    lib = C.CDLL(str(path))
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
+    # the release library reports no device checks, the debug build does
+    assert lib.moe_debug_checks() == (1 if debug else 0)
+
+
+def test_debug_library_rejects_on_the_host_like_the_release_one():
+    if not fp8.DEBUG_LIB_PATH.exists():
+        pytest.skip("libfp8moe_debug.so not built")
+    dbg = fp8.DebugLibrary()
+    assert dbg.checks == 1
+    bad = fp8.dims(0, 256, 512, 8, 2, 0, 16)
+    assert dbg.workspace_bytes(C.byref(bad)) == 0
+    assert dbg.status_str(ERR_DEVICE_CHECK) == b"device check failed (debug build)"
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.ABI_VERSION == 4
+    assert fp8.ABI_VERSION == 5
+    assert fp8._status_str(ERR_DEVICE_CHECK) == b"device check failed (debug build)"
     assert fp8._status_str(0) == b"ok"
     assert fp8._status_str(ERR_WORKSPACE) == b"workspace too small"
     assert fp8._status_str(99) == b"unknown status"
