@@ -1134,6 +1134,64 @@ __device__ __forceinline__ Cols<cols_per_load<Y>()> combine_groups(
   return acc;
 }
 
+// fp16 y in one slab (splits == 1): columns [c0, c0 + NT * 8) of token t, 16
+// bytes of each row per thread.  The slot lookups of a batch of SL slots are
+// requested together, then the rows of the batch's valid slots (a slot's
+// validity is the same for the whole workgroup: no divergence), then the
+// rows are added in slot order -- the operations and their order are those
+// of combine_groups, so both give the same sums bit for bit.
+template <int NT, int SL>
+__device__ __forceinline__ void combine_row16(const RowSpace &rs, const _Float16 *__restrict__ y,
+                                              const int32_t *__restrict__ ids,
+                                              const float *__restrict__ w,
+                                              const int32_t *__restrict__ inv,
+                                              float *__restrict__ out, int t, int c0) {
+  const int d = rs.d, K = rs.k_max, J = K + rs.S;
+  const int c = c0 + (int)threadIdx.x * 8;
+  if (c >= d) return;
+  Cols<8> acc;
+  acc.zero();
+  for (int j0 = 0; j0 < J; j0 += SL) {
+    int row[SL];
+    float wt[SL];
+    bool ok[SL];
+#pragma unroll
+    for (int u = 0; u < SL; ++u) {
+      const int j = j0 + u;
+      if (j < K) {
+        const int p = t * K + j;
+        const int id = ids[p], r = inv[p];
+        wt[u] = w[p];
+        ok[u] = id >= 0;
+        if constexpr (kDebugChecks) ok[u] = ok[u] && dcheck(r >= 0 && r < rs.capacity, kDbgRow);
+        row[u] = ok[u] ? r : 0;
+      } else {  // a shared row (weight 1: 1 * x == x), or past the end
+        wt[u] = 1.0f;
+        ok[u] = j < J;
+        row[u] = ok[u] ? rs.capacity + (j - K) * rs.T + t : 0;
+      }
+    }
+    v8h v[SL];
+#pragma unroll
+    for (int u = 0; u < SL; ++u)
+      if (ok[u]) v[u] = *reinterpret_cast<const v8h *>(y + (size_t)row[u] * d + c);
+#pragma unroll
+    for (int u = 0; u < SL; ++u) {
+      if (ok[u]) {
+        Cols<8> cur;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          cur.v[q] = v4f{(float)v[u][4 * q], (float)v[u][4 * q + 1], (float)v[u][4 * q + 2],
+                         (float)v[u][4 * q + 3]};
+        acc.fma(wt[u], cur);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    *reinterpret_cast<v4f *>(out + (size_t)t * rs.d + c + 4 * q) = acc.v[q];
+}
+
 // Columns [c0, c0 + NT * cols_per_load<Y>()) of token t.
 template <int NT, typename Y>
 __device__ __forceinline__ void combine_chunk(const RowSpace &rs, const Y *__restrict__ y,
