@@ -62,7 +62,7 @@ def log(msg):
 def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--config", default="mixtral", choices=sorted(DEFAULT_T))
     p.add_argument("--tokens", type=int, default=0, help="batch size (default per config)")
@@ -73,8 +73,8 @@ def parse(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     p.add_argument("--points", default="all", choices=["all", "none"],
                    help="also time the other layer shapes (all) or only the selected one (none)")
-    p.add_argument("--point-steps", type=int, default=20)
-    p.add_argument("--point-warmup", type=int, default=10)
+    p.add_argument("--point-steps", type=int, default=50)
+    p.add_argument("--point-warmup", type=int, default=20)
     p.add_argument("--parity-tokens", type=int, default=64,
                    help="tokens of each point compared with the oracle")
     p.add_argument("--no-requant", action="store_true")
