@@ -202,8 +202,8 @@ double expected_items(const moe_dims *d, int32_t msub) {
 // Grouped-GEMM geometry.  A workgroup of W compute waves, each holding nb
 // weight operands of 16 rows (2 or 4), covers W * ch_wave output channels
 // of one work item and one K split.  With nb 2, up to five compute waves
-// and row passes of up to 128 rows, two workgroups share a CU, otherwise
-// one.  A simple model picks (W, nb, splits): workgroups run in whole rounds
+// and row passes of up to 64 rows, the model lets two workgroups share a CU,
+// otherwise one.  A simple model picks (W, nb, splits): workgroups run in whole rounds
 // of resident ones; a CU streams weights at a rate that grows with the
 // weight loads it keeps in flight (resident waves * nb) up to about six
 // two-operand waves; a workgroup's time is proportional to its weight
@@ -261,7 +261,11 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
     for (int W = maxw; W >= 1; --W) {
       if (forced >= 1 && forced <= maxw && W != forced) continue;
       if (msub > 8 && forced < 1 && W != kPfWaves) continue;
-      const int per_cu = (nb == 2 && W <= 5 && msub <= 8) ? 2 : 1;
+      // Two workgroups per CU only for passes of up to 64 rows: with 128-row
+      // passes one workgroup of more waves streamed faster (DeepSeek-shaped
+      // T=512 down projection, 5 waves x 2 -> 7 waves x 1: 72 -> 63 us;
+      // MoE-Prism-shaped gate/up 3 x 2 -> 6 x 1: 82 -> 80 us).
+      const int per_cu = (nb == 2 && W <= 5 && msub <= 4) ? 2 : 1;
       const double slots = (double)kCUs * per_cu;
       const int tiles = (N + W * ch_wave - 1) / (W * ch_wave);
       const double rate = std::min(1.0, W * per_cu * nb / 12.0);
