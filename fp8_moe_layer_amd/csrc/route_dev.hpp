@@ -256,6 +256,86 @@ __device__ __forceinline__ void topk_row_wave_n(const float *l, int E, int k_max
   }
 }
 
+// More than 128 experts: lane l holds the NS consecutive experts NS*l ..
+// NS*l + NS-1, sorted once (a sorting network on (key descending, index
+// ascending)).  A pick is then one wave-wide max over the lanes' first keys
+// and a ballot: among lanes holding the max the lowest lane has the lowest
+// expert indices, and inside a lane equal keys are in index order, so the
+// picks come in the same order as in topk_row_wave_n (logit descending, lower
+// index first) -- the same ids and, accumulated in that order, the same
+// weights -- for a few instructions per pick instead of a scan of every slot.
+template <int NS>
+__device__ __forceinline__ void topk_row_wave_sorted(const float *l, int E, int k_max, int kt,
+                                                     int32_t *__restrict__ ids_row,
+                                                     float *__restrict__ w_row, int lane) {
+  uint32_t key[NS];
+  int idx[NS];
+  {
+    float lv[NS];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      const int e = lane * NS + c;
+      lv[c] = e < E ? l[e] : 0.0f;
+    }
+    if constexpr (kDebugChecks) {
+      bool fin = true;
+#pragma unroll
+      for (int c = 0; c < NS; ++c) fin &= !(lane * NS + c < E) || __builtin_isfinite(lv[c]);
+      dcheck(fin, kDbgNonFinite);
+    }
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      const int e = lane * NS + c;
+      key[c] = e < E ? order_key(lv[c]) : 0u;
+      idx[c] = e;
+    }
+  }
+  // slot i before slot j: larger key, or equal key and lower index
+  auto cmpswap = [&](int i, int j) {
+    const bool sw = key[j] > key[i] || (key[j] == key[i] && idx[j] < idx[i]);
+    const uint32_t ki = key[i], kj = key[j];
+    const int ii = idx[i], ij = idx[j];
+    key[i] = sw ? kj : ki;
+    key[j] = sw ? ki : kj;
+    idx[i] = sw ? ij : ii;
+    idx[j] = sw ? ii : ij;
+  };
+  static_assert(NS == 8, "the sorting network is the 19-comparator one for 8 inputs");
+  cmpswap(0, 2); cmpswap(1, 3); cmpswap(4, 6); cmpswap(5, 7);
+  cmpswap(0, 4); cmpswap(1, 5); cmpswap(2, 6); cmpswap(3, 7);
+  cmpswap(0, 1); cmpswap(2, 3); cmpswap(4, 5); cmpswap(6, 7);
+  cmpswap(2, 4); cmpswap(3, 5);
+  cmpswap(1, 4); cmpswap(3, 6);
+  cmpswap(1, 2); cmpswap(3, 4); cmpswap(5, 6);
+  float m = 0.0f, z = 0.0f, my_eps = 0.0f;
+  int my_id = -1;
+  for (int j = 0; j < kt; ++j) {
+    const uint32_t best = wave_max_u32(key[0]);
+    const uint64_t hold = __ballot(key[0] == best);
+    const int win = (int)__builtin_ctzll(hold);
+    const int e = __builtin_amdgcn_readlane(idx[0], win);
+    const bool pop = lane == win;  // the winner's list moves up by one
+#pragma unroll
+    for (int c = 0; c < NS - 1; ++c) {
+      key[c] = pop ? key[c + 1] : key[c];
+      idx[c] = pop ? idx[c + 1] : idx[c];
+    }
+    key[NS - 1] = pop ? 0u : key[NS - 1];
+    const float lg = key_logit(best);
+    if (j == 0) m = lg;
+    const float eps = expf(lg - m);
+    z += eps;
+    if (lane == j) {
+      my_eps = eps;
+      my_id = e;
+    }
+  }
+  if (lane < k_max) {
+    ids_row[lane] = lane < kt ? my_id : -1;
+    w_row[lane] = lane < kt ? my_eps / z : 0.0f;
+  }
+}
+
 // l: the token's E logits (global memory or LDS); writes the token's k_max
 // slots of ids / w.
 __device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, int kt,
@@ -266,7 +346,7 @@ __device__ __forceinline__ void topk_row_wave(const float *l, int E, int k_max, 
   else if (E <= 2 * kWave)
     topk_row_wave_n<2>(l, E, k_max, kt, ids_row, w_row, lane);
   else
-    topk_row_wave_n<kTopkSlots>(l, E, k_max, kt, ids_row, w_row, lane);
+    topk_row_wave_sorted<kTopkSlots>(l, E, k_max, kt, ids_row, w_row, lane);
 }
 
 __device__ __forceinline__ void topk_token_wave(const float *__restrict__ logits, int T, int E,
