@@ -147,7 +147,11 @@ static __device__ __attribute__((aligned(64))) uint8_t g_zero_piece[64];
 // nothing.
 template <int NB, bool GATEUP, bool NT>
 struct WOperands {
+  // bw: the 2 KB weight tile of the split's first K step for channel group
+  // nb (the same for the whole wave, so it can live in scalar registers);
+  // lane l reads its 16 bytes at l * 16 and 1024 + l * 16 of each tile.
   const uint8_t *bw[NB];
+  int l16;
   int ch[NB];
   float wsc[NB];
   int nks;      // K steps of this split
@@ -160,6 +164,7 @@ struct WOperands {
     const int K = GATEUP ? g.rs.d : g.rs.f;
     const int KT = (K + 127) >> 7;  // weight tiles along K
     nks = nks_;
+    l16 = lane * 16;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       int o;
@@ -178,8 +183,11 @@ struct WOperands {
       const int orow = o < N ? o : N - 1;
       ch[nb] = o;
       wsc[nb] = sbase[ex * N + orow];
-      // tile order: 16 rows x 128 K bytes per 2 KB tile, lane l at l*16 and 1024 + l*16
-      bw[nb] = wbase + ((size_t)(orow >> 4) * KT + (k_begin >> 7)) * 2048 + lane * 16;
+      // tile order: 16 rows x 128 K bytes per 2 KB tile.  c0 is a multiple of
+      // 16 and so is N: a group of 16 channels past N clamps, as a whole, to
+      // the last group (the rows of channel N - 1, as orow)
+      const int grp = min((c0 >> 4) + (GATEUP ? (nb >> 1) : nb), (N >> 4) - 1);
+      bw[nb] = wbase + ((size_t)grp * KT + (k_begin >> 7)) * 2048;
     }
   }
 
@@ -188,7 +196,7 @@ struct WOperands {
   // zero padding of a 64-byte tail step meets zero activation pieces.
   __device__ __forceinline__ void load(v8i (&b)[NB], int ks) const {
     ks = ks < nks ? (ks + rot >= nks ? ks + rot - nks : ks + rot) : nks - 1;
-    const int o0 = ks * 2048;
+    const int o0 = ks * 2048 + l16;
     const int o1 = o0 + 1024;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -565,7 +573,8 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
                 acc[mb + j][nb] = mfma_e4m3_16x16x128(a[j], ring[s][nb], acc[mb + j][nb]);
           }
         }
-        wo.load(ring[s], ks + C::PF);
+        // the pass's last PF steps load nothing (the next pass refills the ring)
+        if (ks + C::PF < nks_pf) wo.load(ring[s], ks + C::PF);
         if ((ks + 1) % C::KSC == 0 || ks + 1 == nks_pf) barrier_lds();  // end of chunk c
       }
     }
@@ -600,7 +609,8 @@ __host__ __device__ constexpr int ares_lds_bytes(int msub, int ksp, int scale_fl
 
 template <int NB, bool GATEUP>
 struct TilePtrs {
-  const uint8_t *bw[NB];
+  const uint8_t *bw[NB];  // tile of K step 0 for channel group nb (wave-uniform)
+  int l16;                // lane * 16: the lane's bytes in each 1 KB half
   int ch[NB];
   int nks;
   // c0: the wave's first output channel (no memory access: addresses only)
@@ -610,6 +620,7 @@ struct TilePtrs {
     const int K = GATEUP ? g.rs.d : g.rs.f;
     const int KT = (K + 127) >> 7;
     nks = nks_;
+    l16 = lane * 16;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       int o;
@@ -622,15 +633,16 @@ struct TilePtrs {
         o = c0 + nb * 16 + (lane & 15);
         wbase = (shared ? g.w.ws_down : g.w.w_down) + ex * (size_t)N * KT * 128;
       }
-      const int orow = o < N ? o : N - 1;
       ch[nb] = o;
-      bw[nb] = wbase + (size_t)(orow >> 4) * KT * 2048 + lane * 16;
+      // c0 and N are multiples of 16: a group past N clamps to the last one
+      const int grp = min((c0 >> 4) + (GATEUP ? (nb >> 1) : nb), (N >> 4) - 1);
+      bw[nb] = wbase + (size_t)grp * KT * 2048;
     }
   }
   template <bool NT>
   __device__ __forceinline__ void load(v8i (&b)[NB], int ks) const {
     ks = ks < nks ? ks : nks - 1;
-    const int o0 = ks * 2048;
+    const int o0 = ks * 2048 + l16;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const v4i lo = NT ? load16_nt(bw[nb] + o0) : load16(bw[nb] + o0);
