@@ -60,12 +60,13 @@ moe_status done(moe_status s, const char *fn) {
   const uint32_t b = debug_take_route() | debug_take_permute() | debug_take_expert() |
                      debug_take_persistent();
   if (b)
-    return fail(MOE_ERR_DEVICE_CHECK, "%s: device checks failed (0x%x):%s%s%s%s%s%s", fn, b,
+    return fail(MOE_ERR_DEVICE_CHECK, "%s: device checks failed (0x%x):%s%s%s%s%s%s%s", fn, b,
                 (b & 1u) ? " k_per_token outside [1, k_max];" : "",
                 (b & 2u) ? " non-finite logit or activation row;" : "",
                 (b & 4u) ? " top-k id outside [-1, E);" : "",
                 (b & 8u) ? " work item outside its expert's rows;" : "",
                 (b & 16u) ? " row index outside the row space;" : "",
+                (b & 32u) ? " GEMM tile channel not a multiple of 16;" : "",
                 (b & 0x80000000u) ? " the check words could not be read;" : "");
 #endif
   return ok();

@@ -36,6 +36,7 @@ enum : uint32_t {
   kDbgTopkId = 1u << 2,     // a top-k id outside [-1, E)
   kDbgPermute = 1u << 3,    // a work item outside the expert row space
   kDbgRow = 1u << 4,        // a sorted pair or combine row index outside its range
+  kDbgTile = 1u << 5,       // a GEMM wave's first weight channel not a multiple of 16
 };
 #ifdef FP8MOE_DEBUG
 constexpr bool kDebugChecks = true;

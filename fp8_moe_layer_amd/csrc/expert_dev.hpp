@@ -165,6 +165,7 @@ struct WOperands {
     const int KT = (K + 127) >> 7;  // weight tiles along K
     nks = nks_;
     l16 = lane * 16;
+    if constexpr (kDebugChecks) dcheck((c0 & 15) == 0, kDbgTile);  // the group clamp below
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       int o;
@@ -621,6 +622,7 @@ struct TilePtrs {
     const int KT = (K + 127) >> 7;
     nks = nks_;
     l16 = lane * 16;
+    if constexpr (kDebugChecks) dcheck((c0 & 15) == 0, kDbgTile);  // the group clamp below
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       int o;

@@ -44,10 +44,11 @@
  *     [1, k_max], an id outside [-1, E) is dropped), but the results are then
  *     undefined.  The debug build of the same sources, libfp8moe_debug.so
  *     (FP8MOE_DEBUG; moe_debug_checks() returns 1), checks them on the
- *     device together with the permutation's index invariants, waits for its
- *     work at the end of every call that enqueues any, and returns
- *     MOE_ERR_DEVICE_CHECK naming the checks that failed.  It synchronises,
- *     so it is not for graph capture or timing.
+ *     device together with the permutation's index invariants and the GEMM
+ *     tiles' channel alignment, waits for its work at the end of every call
+ *     that enqueues any, and returns MOE_ERR_DEVICE_CHECK naming the checks
+ *     that failed.  It synchronises, so it is not for graph capture or
+ *     timing.
  *   - Calls on one stream are ordered; calls on different streams that share
  *     output or workspace buffers race.
  */
