@@ -303,6 +303,7 @@ struct Layout {
   bool nt_gu, nt_dn;  // non-temporal weight loads
   GemmPlan gu, dn;
   bool ares_gu, ares_dn;     // A-resident tiles (short K)
+  bool rq_gu;                // gate/up with the requantisation fused in (f <= 224)
   int32_t ntg_gu, ntg_dn;    // their N-tiles per workgroup
 };
 
@@ -353,10 +354,17 @@ Layout layout_of(const moe_dims *d) {
   L.ares_gu = use_ares(d, L.gu, L.msub_big, true) && L.ntg_gu >= 2;
   L.ares_dn = use_ares(d, L.dn, L.msub_big, false) && L.ntg_dn >= 2;
   L.splits = L.ares_dn ? 1 : L.dn.splits;
+  // Where one workgroup of up to twelve two-operand waves spans all of f, the
+  // gate/up epilogue requantises h itself (no fp32 h, no requantisation
+  // launch), in row passes of at most 64 rows over the same work items (cut
+  // at 16*msub_big rows).  FP8MOE_RQ=0 keeps the separate requantisation.
+  L.rq_gu = !(d->flags & (MOE_F_NO_REQUANT | MOE_F_PERSISTENT)) && !L.ares_gu &&
+            L.msub_big <= 8 && d->f <= 16 * kRqMaxWaves && env_int("FP8MOE_RQ", 1) != 0;
+  if (L.rq_gu) L.gu = GemmPlan{(d->f + 15) / 16, 1, 2};
   {
     int32_t sp, ks;
     down_split_geometry(d->f, L.msub, L.splits, &sp, &ks);
-    L.nt_gu = L.gu.nb == 2 && L.msub <= 8 && stream_weights(d, L.msub_big, d->d);
+    L.nt_gu = (L.gu.nb == 2 || L.rq_gu) && L.msub <= 8 && stream_weights(d, L.msub_big, d->d);
     L.nt_dn = L.dn.nb == 2 && L.msub <= 8 && !(d->flags & MOE_F_NO_REQUANT) &&
               stream_weights(d, L.msub_big, ks);
   }
@@ -549,12 +557,16 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
                                     L.ntg_gu, L.nt_gu, st),
                         "gate_up")))
       return s;
+  } else if (L.rq_gu) {
+    if ((s = hip_status(launch_gate_up_rq(rs, xq, sx, ew, hq, sh, L.msub, L.gu.waves, L.nt_gu, st),
+                        "gate_up")))
+      return s;
   } else if ((s = hip_status(launch_gate_up(rs, xq, sx, ew, h, L.msub, L.msub_big, L.gu.waves, L.gu.nb, L.nt_gu, st), "gate_up"))) {
     return s;
   }
   mark(4);
   if (requant) {
-    if ((s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
+    if (!L.rq_gu && (s = hip_status(launch_requant(rs, h, hq, sh, st), "requant"))) return s;
     mark(5);
     if (L.ares_dn) {
       if ((s = hip_status(launch_ares(rs, hq, sh, ew, nullptr, y16, false, L.msub_big,

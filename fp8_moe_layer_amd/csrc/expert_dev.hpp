@@ -62,6 +62,10 @@ struct GemmArgs {
   // launch's workgroups run in one round they otherwise walk their weight
   // rows in step, every one at the same K offset at the same time.
   int32_t krot = 0;
+  // Gate/up with the requantisation fused into its epilogue (the tile spans
+  // all of f): hq [rows][f] e4m3 codes and hsc [rows] = amax/448 instead of h.
+  uint8_t *hq = nullptr;
+  float *hsc = nullptr;
 };
 
 __device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, int &expert,
@@ -358,6 +362,91 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
   }
 }
 
+// Gate/up epilogue with the per-row requantisation fused in, for a tile that
+// spans all f channels of its rows (W waves of NB/2 channel groups each, the
+// item's rows in one pass).  h = SiLU(g)*u exactly as the h epilogue forms it;
+// each wave's row maxima of |h| over its channels (lanes of one DPP row hold
+// one row's 16 channels of a group) go to LDS, pmax[wave][row]; after one
+// workgroup barrier (the loader wave takes it too) a row's amax is the
+// maximum over the waves, and hq = e4m3(h * (448/amax)), hsc = amax/448 --
+// the separate requantisation's operations on the same h, so the same codes
+// and scales bit for bit, with no fp32 h in memory.  Every row of the pass
+// is written: a padding row has h = 0, so codes 0 and scale 1 (the down
+// projection never reads them).
+template <int MSUB, int NB, bool NT>
+__device__ __forceinline__ void gemm_epilogue_rq(const GemmArgs &g, const v4f (&acc)[MSUB][NB],
+                                                 const WOperands<NB, true, NT> &wo,
+                                                 const float *rsc, float *pmax, int row0, int p0,
+                                                 int prow, int msub, int lane, int wave, int W) {
+  constexpr int MP = 16 * MSUB;
+  const int N = g.rs.f;
+  // the row offsets below are formed here, not hoisted above the K loop
+  // (where they would be held in registers the loop needs)
+  asm volatile("" : "+v"(lane));
+  const int kg = lane >> 4, ln = lane & 15;
+  // h of (row group m, element i, channel group cg), formed from the
+  // accumulators both times it is needed (the same operations, so the same
+  // bits): holding it across the barrier would cost registers the K loop uses
+  auto h_of = [&](int m, int cg, int i, float sxr) {
+    const float gv = acc[m][2 * cg][i] * sxr * wo.wsc[2 * cg];
+    const float uv = acc[m][2 * cg + 1][i] * sxr * wo.wsc[2 * cg + 1];
+    return gv * __builtin_amdgcn_rcpf(1.0f + exp_neg(gv)) * uv;
+  };
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m) {
+    const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float pm = 0.0f;
+#pragma unroll
+      for (int cg = 0; cg < NB / 2; ++cg)
+        if (wo.ch[2 * cg] < N) pm = fmaxf(pm, fabsf(h_of(m, cg, i, sx4[i])));
+      // the row's maximum over the 16 lanes of this DPP row
+      pm = fmaxf(pm, dpp_mov<kDppQuadXor1>(pm));
+      pm = fmaxf(pm, dpp_mov<kDppQuadXor2>(pm));
+      pm = fmaxf(pm, dpp_mov<kDppHalfMirror>(pm));
+      pm = fmaxf(pm, dpp_mov<kDppMirror>(pm));
+      if (ln == 0) pmax[wave * MP + m * 16 + kg * 4 + i] = pm;
+    }
+    // one row group at a time: interleaving the groups' SiLU chains would
+    // raise register pressure past the K loop's
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  barrier_lds();
+  const bool full = prow == MP;
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m) {
+    if (m < msub) {
+      const v4f sx4 = *reinterpret_cast<const v4f *>(rsc + m * 16 + kg * 4);
+      const int rlim = full ? 4 : prow - (m * 16 + kg * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m * 16 + kg * 4 + i;
+        if (m < msub - 1 || i < rlim) {
+          float amax = pmax[r];
+          for (int w = 1; w < W; ++w) amax = fmaxf(amax, pmax[w * MP + r]);
+          float rq = 1.0f, sq = 1.0f;
+          if (amax != 0.0f) {
+            rq = kE4m3Max / amax;
+            sq = amax / kE4m3Max;
+          }
+          uint8_t *q = g.hq + (size_t)(row0 + p0 + r) * N;
+#pragma unroll
+          for (int cg = 0; cg < NB / 2; ++cg) {
+            if (wo.ch[2 * cg] < N) {
+              const float hv = h_of(m, cg, i, sx4[i]);
+              if constexpr (kDebugChecks) dcheck(__builtin_isfinite(hv), kDbgNonFinite);
+              q[wo.ch[2 * cg]] = (uint8_t)(e4m3x4(hv * rq, 0.0f, 0.0f, 0.0f) & 0xffu);
+            }
+          }
+          if (wave == 0 && ln == 0) g.hsc[row0 + p0 + r] = sq;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 
 template <int MSUB>
@@ -377,6 +466,9 @@ struct Chunk {
   // flight, so the epilogue needs no global loads on its critical path.
   static constexpr int RING = NBUF * BYTES;
   static constexpr int LDS = RING + 2 * MP * (int)sizeof(float);
+  // with the fused requantisation: + the waves' row maxima (pmax[wave][row],
+  // up to 12 waves)
+  static constexpr int LDS_RQ = LDS + 12 * MP * (int)sizeof(float);
 };
 
 // LDS of the persistent kernel's GEMM phases (row passes of up to 128 rows).
@@ -407,7 +499,10 @@ __device__ __forceinline__ void loader_wait_barrier(int chunks_in_flight) {
 // early (uniformly) for an empty item.
 // NT: the weight loads carry the non-temporal hint, so that a weight stream
 // read once does not push the activation rows and row tables out of L2.
-template <int MSUB, int NB, bool GATEUP, bool NT = false>
+// RQ (gate/up, the tile spanning all f): the requantisation is fused into
+// the epilogue (gemm_epilogue_rq); abuf then holds Chunk<MSUB>::LDS_RQ bytes
+// and every wave, the loader included, takes one more barrier per pass.
+template <int MSUB, int NB, bool GATEUP, bool NT = false, bool RQ = false>
 __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t *abuf) {
   using C = Chunk<MSUB>;
   static_assert(C::LPC == 16 && C::NBUF == 4, "loader_wait_barrier assumes 16 loads per chunk");
@@ -520,6 +615,7 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
         const int newest = min(c + C::NBUF - 1, nchunks - 1);
         loader_wait_barrier(newest - (c + 1));  // chunk c+1 landed
       }
+      if constexpr (RQ) barrier_lds();  // the compute waves' row-maximum exchange
     }
     return;
   }
@@ -580,7 +676,13 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
       }
     }
 
-    gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
+    if constexpr (RQ) {
+      static_assert(GATEUP, "the fused requantisation follows the gate/up GEMM");
+      gemm_epilogue_rq<MSUB, NB, NT>(g, acc, wo, rsc, reinterpret_cast<float *>(abuf + C::LDS), row0,
+                                     p0, prow, msub, lane, wave, W);
+    } else {
+      gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
+    }
   }
 }
 

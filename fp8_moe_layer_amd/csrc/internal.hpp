@@ -99,6 +99,13 @@ constexpr int kPfWaves = 8;  // prefill GEMM: 256-row passes, every wave gathers
 hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx,
                           const ExpertWeights &w, float *h, int32_t msub, int32_t msub_big,
                           int32_t waves, int32_t nb, bool stream_weights, hipStream_t stream);
+// Gate/up with the requantisation fused into its epilogue, for f <= 16 *
+// kRqMaxWaves: one workgroup of `waves` two-operand compute waves (waves * 16
+// >= f) per work item writes hq and sh (every row of the item) instead of h.
+constexpr int kRqMaxWaves = 12;
+hipError_t launch_gate_up_rq(const RowSpace &rs, const uint8_t *xq, const float *sx,
+                             const ExpertWeights &w, uint8_t *hq, float *sh, int32_t msub,
+                             int32_t waves, bool stream_weights, hipStream_t stream);
 // Per-row e4m3 requantisation of h (real rows only): hq codes, sh = amax/448.
 hipError_t launch_requant(const RowSpace &rs, const float *h, uint8_t *hq, float *sh,
                           hipStream_t stream);

@@ -53,6 +53,17 @@ __global__ __launch_bounds__(MSUB > 8 || NB > 2 ? kGemmMaxThreadsWide : kGemmMax
   wsgemm_tile<MSUB, NB, GATEUP, NT>(g, blockIdx.x, abuf);
 }
 
+// Gate/up with the per-row requantisation fused into the epilogue: W compute
+// waves of two weight operands (16 h channels each, W <= 12) span all
+// f <= 192 channels of an item's rows, so the workgroup holds every h value
+// of its rows and writes e4m3 codes and row scales instead of fp32 h.  Row
+// passes of at most 64 rows keep 13 waves within 128 VGPRs each.
+template <int MSUB, bool NT>
+__global__ __launch_bounds__((kRqMaxWaves + 1) * 64) void wsgemm_rq_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t abuf[Chunk<MSUB>::LDS_RQ];
+  wsgemm_tile<MSUB, 2, true, NT, true>(g, blockIdx.x, abuf);
+}
+
 // Prefill-sized batches: 256-row passes, eight waves that all gather and
 // compute (one workgroup per CU: 256 VGPRs per wave, 66 KB of LDS).
 // Workgroups are dealt to the eight XCDs in turn (workgroup i to XCD i % 8),
@@ -314,6 +325,32 @@ hipError_t launch_gate_up(const RowSpace &rs, const uint8_t *xq, const float *sx
   }
   return stream_weights ? launch_nb2<true, true>(g, msub, msub_big, waves, stream)
                         : launch_nb2<true, false>(g, msub, msub_big, waves, stream);
+}
+
+template <int MSUB>
+static hipError_t launch_rq_t(const GemmArgs &g, int waves, bool nt, hipStream_t stream) {
+  const int blocks = grid_items(g.rs);  // one tile: the workgroup spans f
+  if (blocks == 0) return hipSuccess;
+  if (nt)
+    wsgemm_rq_kernel<MSUB, true><<<blocks, (waves + 1) * 64, 0, stream>>>(g);
+  else
+    wsgemm_rq_kernel<MSUB, false><<<blocks, (waves + 1) * 64, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_rq(const RowSpace &rs, const uint8_t *xq, const float *sx,
+                             const ExpertWeights &w, uint8_t *hq, float *sh, int32_t msub,
+                             int32_t waves, bool stream_weights, hipStream_t stream) {
+  if (waves < 1 || waves > kRqMaxWaves || waves * 16 < rs.f || msub < 1)
+    return hipErrorInvalidValue;  // the host plans only tiles that span f
+  GemmArgs g{rs, xq, sx, nullptr, w, nullptr, 1, rs.d};
+  g.hq = hq;
+  g.hsc = sh;
+  // an item longer than the pass takes several passes (each row's amax
+  // still spans the workgroup's channels)
+  if (msub >= 4) return launch_rq_t<4>(g, waves, stream_weights, stream);
+  if (msub >= 2) return launch_rq_t<2>(g, waves, stream_weights, stream);
+  return launch_rq_t<1>(g, waves, stream_weights, stream);
 }
 
 // Rows of up to 4096 values: a wave per row, four rows per workgroup.
