@@ -1251,49 +1251,47 @@ __device__ __forceinline__ Cols<cols_per_load<Y>()> combine_groups(
 }
 
 // fp16 y in one slab (splits == 1): columns [c0, c0 + NT * 8) of token t, 16
-// bytes of each row per thread.  The slot lookups of a batch of SL slots are
-// requested together, then the rows of the batch's valid slots (a slot's
-// validity is the same for the whole workgroup: no divergence), then the
-// rows are added in slot order -- the operations and their order are those
-// of combine_groups, so both give the same sums bit for bit.
+// bytes of each row per thread.  A slot's validity is the same for the whole
+// workgroup (no divergence); rows are added in slot order, then the shared
+// experts' -- the operations and their order are those of combine_groups, so
+// both give the same sums bit for bit.
 template <int NT, int SL>
 __device__ __forceinline__ void combine_row16(const RowSpace &rs, const _Float16 *__restrict__ y,
                                               const int32_t *__restrict__ ids,
                                               const float *__restrict__ w,
                                               const int32_t *__restrict__ inv,
                                               float *__restrict__ out, int t, int c0) {
-  const int d = rs.d, K = rs.k_max, J = K + rs.S;
+  const int d = rs.d, K = rs.k_max;
+  const int lane = (int)threadIdx.x & 63;
+  // Every slot's lookups at once: lane j of each wave holds slot j's row and
+  // weight (k_max <= 32), the valid slots are a ballot; then their rows are
+  // requested SL at a time (wave-uniform row indices from v_readlane) and
+  // added in slot order, then the shared experts' rows -- the same sums as
+  // slot-by-slot, in one lookup latency plus one per SL valid slots.
+  int my_row = 0;
+  float my_w = 0.0f;
+  bool my_ok = false;
+  if (lane < K) {
+    const int p = t * K + lane;
+    const int id = ids[p], r = inv[p];
+    my_w = w[p];
+    my_ok = id >= 0;
+    if constexpr (kDebugChecks) my_ok = my_ok && dcheck(r >= 0 && r < rs.capacity, kDbgRow);
+    my_row = my_ok ? r : 0;
+  }
+  uint64_t pending = __builtin_amdgcn_ballot_w64(my_ok);
   const int c = c0 + (int)threadIdx.x * 8;
-  if (c >= d) return;
+  const bool live = c < d;
   Cols<8> acc;
   acc.zero();
-  for (int j0 = 0; j0 < J; j0 += SL) {
-    int row[SL];
-    float wt[SL];
-    bool ok[SL];
-#pragma unroll
-    for (int u = 0; u < SL; ++u) {
-      const int j = j0 + u;
-      if (j < K) {
-        const int p = t * K + j;
-        const int id = ids[p], r = inv[p];
-        wt[u] = w[p];
-        ok[u] = id >= 0;
-        if constexpr (kDebugChecks) ok[u] = ok[u] && dcheck(r >= 0 && r < rs.capacity, kDbgRow);
-        row[u] = ok[u] ? r : 0;
-      } else {  // a shared row (weight 1: 1 * x == x), or past the end
-        wt[u] = 1.0f;
-        ok[u] = j < J;
-        row[u] = ok[u] ? rs.capacity + (j - K) * rs.T + t : 0;
-      }
-    }
+  auto add_rows = [&](const int (&row)[SL], const float (&wt)[SL], int n) {
     v8h v[SL];
 #pragma unroll
     for (int u = 0; u < SL; ++u)
-      if (ok[u]) v[u] = *reinterpret_cast<const v8h *>(y + (size_t)row[u] * d + c);
+      if (u < n && live) v[u] = *reinterpret_cast<const v8h *>(y + (size_t)row[u] * d + c);
 #pragma unroll
     for (int u = 0; u < SL; ++u) {
-      if (ok[u]) {
+      if (u < n) {
         Cols<8> cur;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
@@ -1302,7 +1300,37 @@ __device__ __forceinline__ void combine_row16(const RowSpace &rs, const _Float16
         acc.fma(wt[u], cur);
       }
     }
+  };
+  while (pending) {  // routed slots, ascending
+    int row[SL];
+    float wt[SL];
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < SL; ++u) {
+      row[u] = 0;
+      wt[u] = 0.0f;
+      if (pending) {
+        const int j = (int)__builtin_ctzll(pending);
+        pending &= pending - 1;
+        row[u] = readlane(my_row, j);
+        wt[u] = readlane(my_w, j);
+        n = u + 1;
+      }
+    }
+    add_rows(row, wt, n);
   }
+  for (int s0 = 0; s0 < rs.S; s0 += SL) {  // shared experts, weight 1 (1 * x == x)
+    int row[SL];
+    float wt[SL];
+    const int n = min(SL, rs.S - s0);
+#pragma unroll
+    for (int u = 0; u < SL; ++u) {
+      row[u] = rs.capacity + (s0 + u) * rs.T + t;
+      wt[u] = 1.0f;
+    }
+    add_rows(row, wt, n);
+  }
+  if (!live) return;
 #pragma unroll
   for (int q = 0; q < 2; ++q)
     *reinterpret_cast<v4f *>(out + (size_t)t * rs.d + c + 4 * q) = acc.v[q];

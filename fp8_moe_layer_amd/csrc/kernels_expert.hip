@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void combine_row_kernel(RowSpace rs, const _Fl
                                                           const float *__restrict__ w,
                                                           const int32_t *__restrict__ inv,
                                                           float *__restrict__ out) {
-  combine_row16<256, 8>(rs, y, ids, w, inv, out, blockIdx.x, blockIdx.y * 256 * 8);
+  combine_row16<256, 16>(rs, y, ids, w, inv, out, blockIdx.x, blockIdx.y * 256 * 8);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -428,11 +428,9 @@ hipError_t launch_combine(const RowSpace &rs, const float *y, const _Float16 *y1
   // one fp16 slab: 16-byte row pieces, a token's 2048 columns per workgroup
   // (prefill-sized batches measured 27-33 % faster than four columns per
   // thread -- DeepSeek-shaped T=8192 95 -> 66 us -- decode sizes the same).
-  // FP8MOE_COMBINE_ROW_T: the smallest batch that takes it (tile tuning).
-  static const int row_min_t = [] {
-    const char *v = getenv("FP8MOE_COMBINE_ROW_T");
-    return (v && *v) ? atoi(v) : 1;
-  }();
+  // FP8MOE_COMBINE_ROW_T: the smallest batch that takes it (tile tuning, tests).
+  const char *row_env = getenv("FP8MOE_COMBINE_ROW_T");
+  const int row_min_t = (row_env && *row_env) ? atoi(row_env) : 1;
   if (y16 && splits == 1 && rs.T >= row_min_t)
     combine_row_kernel<<<dim3(rs.T, (rs.d + 2047) / 2048), 256, 0, stream>>>(rs, y16, ids, w,
                                                                             inv_pairs, out);

@@ -109,3 +109,26 @@ def test_fused_requant_prism_full_size(monkeypatch):
     assert torch.equal(ia, ib)
     assert torch.equal(a, b), f"max |diff| {(a - b).abs().max().item():.3e}"
     assert np.isfinite(to_np(a)).all()
+
+
+COMBINE_SPECS = {
+    "prism-like": wl.TINY.with_(T=90, d=2048, f=192, E=64, k=32, k_choices=(4, 8, 16, 32)),
+    "shared": wl.TINY.with_(T=40, d=256, f=192, E=8, k=2, n_shared=2),
+    "ragged-d": wl.TINY.with_(T=33, d=320, f=512, E=16, k=6, n_shared=1),
+}
+
+
+@pytest.mark.parametrize("name", list(COMBINE_SPECS))
+def test_combine_row_kernel_bit_exact(name, monkeypatch):
+    """The one-slab combine (every slot lookup of a token at once, the valid
+    slots' rows SL at a time) adds the same rows in the same order as the
+    slot-group combine, so the layer output is the same bit for bit with
+    either (FP8MOE_COMBINE_ROW_T=1: always the one-slab kernel; 10**9:
+    never), with per-token k, shared experts and a ragged d."""
+    L = Layer(COMBINE_SPECS[name], want_oracle=False)
+    monkeypatch.setenv("FP8MOE_DOWN_SPLITS", "1")
+    outs = []
+    for row_t in ("1", str(10 ** 9)):
+        monkeypatch.setenv("FP8MOE_COMBINE_ROW_T", row_t)
+        outs.append(_forward(L, L.spec.T, True, monkeypatch)[0])
+    assert torch.equal(outs[0], outs[1]), f"max |diff| {(outs[0] - outs[1]).abs().max().item():.3e}"
