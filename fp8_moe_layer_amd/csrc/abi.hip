@@ -180,15 +180,19 @@ int32_t choose_msub_big(const moe_dims *d, int32_t msub) {
 
 // Non-temporal weight loads pay off where each weight byte is read by one
 // workgroup (every expert's rows, routed and shared, expected in one work
-// item) over a long enough K range (measured: K >= 2048 bytes gains, short
-// ranges and weights re-read by several items lose).
-bool stream_weights(const moe_dims *d, int32_t msub_big, int32_t kbytes) {
+// item); weights re-read by several items lose.  The K range itself does not
+// matter: with the hint on the short-K down projections as well (an earlier
+// rule asked for K >= 2048 bytes) the MoE-Prism-shaped layer (K = 192, the
+// A-resident tile) went 261 -> 246 us and the Qwen3-shaped T=64 layer at 16
+// distinct experts (K = 768) 53.2 -> 51.5 us; Qwen3 T=64 at ~127 experts and
+// DeepSeek T=32 (K = 1408) stayed within 1 %.
+bool stream_weights(const moe_dims *d, int32_t msub_big) {
   const int forced = env_int("FP8MOE_NT", -1);  // tile-tuning override
   if (forced == 0 || forced == 1) return forced == 1;
   const double mean = (double)d->T * d->k_max / d->E;
   const double est = mean + 4.0 * sqrt(mean) + 2.0;
   const int64_t chunk = 16 * (int64_t)msub_big;
-  return est <= chunk && (d->n_shared == 0 || d->T <= chunk) && kbytes >= 2048;
+  return est <= chunk && (d->n_shared == 0 || d->T <= chunk);
 }
 
 // Expected work items of the grouped GEMMs (rows cut into 16*msub chunks).
@@ -361,13 +365,9 @@ Layout layout_of(const moe_dims *d) {
   L.rq_gu = !(d->flags & (MOE_F_NO_REQUANT | MOE_F_PERSISTENT)) && !L.ares_gu &&
             L.msub_big <= 8 && d->f <= 16 * kRqMaxWaves && env_int("FP8MOE_RQ", 1) != 0;
   if (L.rq_gu) L.gu = GemmPlan{(d->f + 15) / 16, 1, 2};
-  {
-    int32_t sp, ks;
-    down_split_geometry(d->f, L.msub, L.splits, &sp, &ks);
-    L.nt_gu = (L.gu.nb == 2 || L.rq_gu) && L.msub <= 8 && stream_weights(d, L.msub_big, d->d);
-    L.nt_dn = L.dn.nb == 2 && L.msub <= 8 && !(d->flags & MOE_F_NO_REQUANT) &&
-              stream_weights(d, L.msub_big, ks);
-  }
+  L.nt_gu = (L.gu.nb == 2 || L.rq_gu) && L.msub <= 8 && stream_weights(d, L.msub_big);
+  L.nt_dn = L.dn.nb == 2 && L.msub <= 8 && !(d->flags & MOE_F_NO_REQUANT) &&
+            stream_weights(d, L.msub_big);
   L.max_items = max_work_items(d->T, d->E, d->k_max, d->block_m, d->n_shared, L.row_chunk);
   const size_t T = d->T, P = (size_t)d->T * d->k_max, R = L.rows_total;
   size_t o = 0;
@@ -766,7 +766,7 @@ moe_status moe_expert_gate_up(const moe_dims *dims, int32_t capacity, const uint
   const int32_t msub = choose_msub(dims);
   const GemmPlan gp = plan_gemm(dims, msub, true);
   const int32_t mbig = gp.nb == 2 ? choose_msub_big(dims, msub) : msub;
-  const bool nt = gp.nb == 2 && msub <= 8 && stream_weights(dims, mbig, dims->d);
+  const bool nt = gp.nb == 2 && msub <= 8 && stream_weights(dims, mbig);
   s = hip_status(launch_gate_up(rs, xq, sx, to_internal(w), h, msub, mbig, gp.waves, gp.nb, nt,
                                 as_stream(stream)),
                  fn);
@@ -790,9 +790,7 @@ moe_status moe_expert_down(const moe_dims *dims, int32_t capacity, const uint8_t
   const int32_t msub = choose_msub(dims);
   const GemmPlan dp = plan_gemm(dims, msub, false);
   const int32_t mbig = dp.nb == 2 ? choose_msub_big(dims, msub) : msub;
-  int32_t sp, ks;
-  down_split_geometry(dims->f, msub, 1, &sp, &ks);
-  const bool nt = !f32 && dp.nb == 2 && msub <= 8 && stream_weights(dims, mbig, ks);
+  const bool nt = !f32 && dp.nb == 2 && msub <= 8 && stream_weights(dims, mbig);
   s = hip_status(launch_down(rs, f32 ? nullptr : hq, sh, f32 ? h : nullptr, to_internal(w), y, nullptr,
                              msub, mbig, 1, dp.waves, dp.nb, nt, as_stream(stream)),
                  fn);
