@@ -253,7 +253,9 @@ size_t moe_workspace_bytes(const moe_dims *dims /*host*/);
  * requantisation, down projection, weighted combine.  Intermediates stay in
  * the workspace: h in fp32, hq in e4m3, and the down projection's outputs y
  * in fp16 on their way to the combine (values beyond +-65504 saturate; with
- * MOE_F_NO_REQUANT, h and y stay fp32).
+ * MOE_F_NO_REQUANT, h and y stay fp32).  Where one workgroup spans all of f
+ * (f <= 192) the requantisation is done in the gate/up epilogue and h never
+ * reaches memory; hq and its scales are the same bit for bit.
  * x [T][d] fp32; w_router [E][d] (may be NULL when logits_override is given);
  * router_bias [E] or NULL; k_per_token [T] or NULL (all k_max);
  * logits_override [T][E] or NULL; out [T][d] fp32;
@@ -336,7 +338,8 @@ moe_status moe_k_tiers(const int32_t *k_per_token /*host*/, int32_t n, int32_t b
  * that also records stage_events[i] on its stream just before stage i
  * (0 quantise + router logits, 1 top-k, 2 permutation, 3 gate/up,
  * 4 requantisation, 5 down, 6 combine) and stage_events[7] after the last
- * one.  stage_events: host array of n_events >= MOE_N_STAGE_EVENTS hipEvent_t
+ * one; a stage fused into the one before it (top-k into routing, the
+ * requantisation into gate/up) has its two events back to back.  stage_events: host array of n_events >= MOE_N_STAGE_EVENTS hipEvent_t
  * handles created and owned by the caller, or NULL (then identical to
  * moe_fused_forward).  The library records the events during this call only
  * and keeps nothing.  Returns MOE_ERR_SHAPE when stage_events is given with
