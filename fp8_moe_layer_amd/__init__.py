@@ -62,6 +62,9 @@ _router_logits = _sig("moe_router_logits", _i32, _vp, _vp, _vp, _i32, _i32, _i32
 _route_topk = _sig("moe_route_topk", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 _capacity = _sig("moe_capacity", C.c_int64, _i32, _i32, _i32, _i32)
 _permute = _sig("moe_permute", _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp)
+_permute_ws_bytes = _sig("moe_permute_workspace_bytes", C.c_size_t, _i32, _i32, _i32)
+_permute_ws = _sig("moe_permute_ws", _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                   _vp, _vp, C.c_size_t, _vp)
 _gate_up = _sig("moe_expert_gate_up", _i32, _DP, _i32, _vp, _vp, _vp, _vp, _WP, _vp, _vp)
 _down = _sig("moe_expert_down", _i32, _DP, _i32, _vp, _vp, _vp, _vp, _vp, _WP, _vp, _vp)
 _combine = _sig("moe_combine", _i32, _DP, _i32, _vp, _vp, _vp, _vp, _vp, _vp)
@@ -218,16 +221,31 @@ def capacity(T: int, E: int, k_max: int, block_m: int) -> int:
     return int(_capacity(T, E, k_max, block_m))
 
 
-def permute(topk_ids, E: int, block_m: int, cap: Optional[int] = None, stream=None) -> dict:
+def permute_workspace_bytes(T: int, E: int, k_max: int) -> int:
+    return int(_permute_ws_bytes(T, E, k_max))
+
+
+def permute(topk_ids, E: int, block_m: int, cap: Optional[int] = None, stream=None,
+            workspace: bool = False) -> dict:
+    """moe_permute, or with workspace=True moe_permute_ws on a workspace
+    allocated here (the two-launch form for large batches)."""
     T, K = topk_ids.shape
     cap = capacity(T, E, K, block_m) if cap is None else cap
     dev = topk_ids.device
     z = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
     out = dict(sorted_pairs=z(cap), expert_offsets=z(E + 1), block_expert=z((cap + block_m - 1) // block_m),
                inv_pairs=z(T * K), n_blocks=z(1))
-    _check(_permute(_ptr(topk_ids, torch.int32), T, E, K, block_m, cap, _ptr(out["sorted_pairs"]),
-                    _ptr(out["expert_offsets"]), _ptr(out["block_expert"]), _ptr(out["inv_pairs"]),
-                    _ptr(out["n_blocks"]), _stream(stream)))
+    args = (_ptr(topk_ids, torch.int32), T, E, K, block_m, cap, _ptr(out["sorted_pairs"]),
+            _ptr(out["expert_offsets"]), _ptr(out["block_expert"]), _ptr(out["inv_pairs"]),
+            _ptr(out["n_blocks"]))
+    if workspace:
+        n = permute_workspace_bytes(T, E, K)
+        with _on(stream):
+            ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        _check(_permute_ws(*args, _ptr(ws), n, _stream(stream)))
+        out["workspace"] = ws  # kept alive with the outputs until the caller syncs
+    else:
+        _check(_permute(*args, _stream(stream)))
     out["capacity"] = cap
     return out
 

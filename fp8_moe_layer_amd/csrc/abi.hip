@@ -302,7 +302,7 @@ GemmPlan plan_gemm(const moe_dims *d, int32_t msub, bool gate_up) {
 // Workspace layout of moe_fused_forward (all pieces 256-byte aligned).
 struct Layout {
   size_t bar, xq, sx, logits, ids, w, sorted, offsets, block_expert, inv, n_blocks, items, n_items, h,
-      hq, sh, y, total;
+      hq, sh, y, pcnt, total;
   int32_t capacity, rows_total, max_items, row_chunk, msub, msub_big, splits;
   bool nt_gu, nt_dn;  // non-temporal weight loads
   GemmPlan gu, dn;
@@ -394,6 +394,7 @@ Layout layout_of(const moe_dims *d) {
   L.sh = take(R * 4);
   // the fused path keeps y in fp16 (fp32 in the no-requant accuracy mode)
   L.y = take((size_t)L.splits * R * d->d * ((d->flags & MOE_F_NO_REQUANT) ? 4 : 2));
+  L.pcnt = take((size_t)permute_counts_ints(d->T, d->E, d->k_max) * 4);  // slice counts
   L.total = o;
   return L;
 }
@@ -543,7 +544,8 @@ moe_status enqueue_forward(const moe_dims *dims, const float *x, const float *w_
   mark(2);
   if ((s = hip_status(launch_permute(ids, dims->T, dims->E, dims->k_max, dims->block_m, L.capacity,
                                      sorted, offsets, block_expert, inv, n_blocks, items, n_items,
-                                     L.row_chunk, dims->n_shared, st),
+                                     L.row_chunk, dims->n_shared, st,
+                                     reinterpret_cast<int32_t *>(ws + L.pcnt)),
                       "permute")))
     return s;
   RowSpace rs = row_space(dims, L.capacity, sorted, offsets);
@@ -718,11 +720,11 @@ moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k_m
   return done(s, fn);
 }
 
-moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
-                       int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
-                       int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
-                       int32_t *n_blocks, void *stream) {
-  const char *fn = "moe_permute";
+static moe_status permute_checked(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
+                                  int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
+                                  int32_t *expert_offsets, int32_t *block_expert,
+                                  int32_t *inv_pairs, int32_t *n_blocks, int32_t *counts,
+                                  void *stream, const char *fn) {
   if (!topk_ids || !sorted_pairs || !expert_offsets || !block_expert || !inv_pairs || !n_blocks)
     return fail(MOE_ERR_NULL, "%s: every array is required", fn);
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k_max < 1 || k_max > MOE_MAX_K ||
@@ -733,9 +735,40 @@ moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_
                 (long long)capacity_of(T, E, k_max, block_m));
   moe_status s = hip_status(launch_permute(topk_ids, T, E, k_max, block_m, capacity, sorted_pairs,
                                            expert_offsets, block_expert, inv_pairs, n_blocks,
-                                           nullptr, nullptr, 0, 0, as_stream(stream)),
+                                           nullptr, nullptr, 0, 0, as_stream(stream), counts),
                             fn);
   return done(s, fn);
+}
+
+moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
+                       int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
+                       int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
+                       int32_t *n_blocks, void *stream) {
+  return permute_checked(topk_ids, T, E, k_max, block_m, capacity, sorted_pairs, expert_offsets,
+                         block_expert, inv_pairs, n_blocks, nullptr, stream, "moe_permute");
+}
+
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k_max) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k_max < 1 || k_max > MOE_MAX_K ||
+      (int64_t)T * k_max >= ((int64_t)1 << 30))
+    return 0;
+  return (size_t)permute_counts_ints(T, E, k_max) * 4;
+}
+
+moe_status moe_permute_ws(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
+                          int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
+                          int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
+                          int32_t *n_blocks, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  const char *fn = "moe_permute_ws";
+  const size_t need = moe_permute_workspace_bytes(T, E, k_max);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu", fn, workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(MOE_ERR_ALIGN, "%s: the workspace must be 16-byte aligned", fn);
+  return permute_checked(topk_ids, T, E, k_max, block_m, capacity, sorted_pairs, expert_offsets,
+                         block_expert, inv_pairs, n_blocks,
+                         need > 0 ? static_cast<int32_t *>(workspace) : nullptr, stream, fn);
 }
 
 

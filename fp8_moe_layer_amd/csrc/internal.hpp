@@ -73,11 +73,15 @@ hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k_max,
                        const int32_t *k_per_token, int32_t *ids, float *w, hipStream_t stream);
 // items/n_items/row_chunk: optional work list for the expert stages (row_chunk
 // rows per item); pass items == nullptr to skip it.
+// counts: NULL, or permute_counts_ints(T, E, k_max) ints that nothing else
+// writes while the work runs; with them a batch of four or more 1024-pair
+// slices takes two launches instead of three (the same outputs).
+int64_t permute_counts_ints(int32_t T, int32_t E, int32_t k_max);
 hipError_t launch_permute(const int32_t *ids, int32_t T, int32_t E, int32_t k_max, int32_t block_m,
                           int32_t capacity, int32_t *sorted_pairs, int32_t *expert_offsets,
                           int32_t *block_expert, int32_t *inv_pairs, int32_t *n_blocks,
                           WorkItem *items, int32_t *n_items, int32_t row_chunk, int32_t n_shared,
-                          hipStream_t stream);
+                          hipStream_t stream, int32_t *counts = nullptr);
 int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int32_t n_shared,
                        int32_t row_chunk);
 

@@ -22,8 +22,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 }
 
 // ------------------------------------------------------------------ many workgroups
+// Slice s's count of expert e goes to counts[s * stride + e]: into the
+// slice's own inv_pairs range (stride kSlice) for the three-launch path, or
+// into a workspace of its own (stride E) for the two-launch path.
 __global__ __launch_bounds__(kSliceWaves * kWave) void permute_count_kernel(
-    const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ inv_pairs) {
+    const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ counts, int stride) {
   __shared__ int cnt[kSliceWaves * kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int b0, b1;
@@ -41,7 +44,7 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_count_kernel(
     int t = 0;
 #pragma unroll
     for (int w = 0; w < kSliceWaves; ++w) t += c[w];
-    inv_pairs[b0 + e] = t;  // this slice's count of expert e
+    counts[blockIdx.x * stride + e] = t;  // this slice's count of expert e
   }
 }
 
@@ -151,6 +154,65 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void permute_scatter_kernel(
 
 constexpr int kManySlices = 4;  // at least this many slices: the multi-workgroup path
 
+// Layout and scatter in one launch (after permute_count_kernel wrote every
+// slice's counts to `counts`, a buffer nothing else writes): each slice's
+// workgroup reads all the counts, forms the per-expert totals, the padded
+// segment offsets and its own slice's first rows, writes its share of the
+// layout arrays (workgroup 0 also the offsets and the work list) and
+// scatters its slice -- the rows and arrays of the three-launch path,
+// without the single-workgroup layout launch between count and scatter.
+__global__ __launch_bounds__(kSliceWaves * kWave) void permute_layout_scatter_kernel(
+    const int32_t *__restrict__ ids, int P, int E, int bm, int capacity,
+    const int32_t *__restrict__ counts, int32_t *__restrict__ sorted_pairs,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ block_expert,
+    int32_t *__restrict__ inv_pairs, int32_t *__restrict__ n_blocks, WorkItem *__restrict__ items,
+    int32_t *__restrict__ n_items, int row_chunk, int T, int S) {
+  constexpr int NT = kSliceWaves * kWave;
+  __shared__ int cnt[kSliceWaves * kMaxExperts], tot[kMaxExperts], base[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1], item_off[kMaxExperts + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ns = permute_slices(P), me = blockIdx.x;
+  // totals, and the counts of the slices before this one
+  for (int e = tid; e < E; e += NT) {
+    int t = 0, before = 0;
+#pragma unroll 8
+    for (int sl = 0; sl < ns; ++sl) {
+      const int c = counts[sl * E + e];
+      before += sl < me ? c : 0;
+      t += c;
+    }
+    tot[e] = t;
+    base[e] = before;
+  }
+  __syncthreads();
+  layout_offsets<NT>(tot, off, item_off, E, bm, row_chunk);
+  layout_write<NT>(tot, off, item_off, P, E, bm, capacity, sorted_pairs, expert_offsets,
+                   block_expert, n_blocks, items, n_items, row_chunk, T, S, me, ns);
+  // this slice: each wave's count, then rows from the slice's first row per expert
+  int b0, b1;
+  slice_range(P, me, b0, b1);
+  const int per = (b1 - b0 + kSliceWaves - 1) / kSliceWaves;
+  const int w0 = min(b1, b0 + wave * per), w1 = min(b1, w0 + per);
+  const int nbits = expert_bits(E);
+  for (int e = lane; e < E; e += kWave) cnt[wave * E + e] = 0;  // this wave's row
+  __builtin_amdgcn_wave_barrier();
+  slice_count(ids, w0, w1, E, nbits, cnt + wave * E, lane);
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int c[kSliceWaves];
+#pragma unroll
+    for (int w = 0; w < kSliceWaves; ++w) c[w] = cnt[w * E + e];
+    int r = off[e] + base[e];
+#pragma unroll
+    for (int w = 0; w < kSliceWaves; ++w) {
+      cnt[w * E + e] = r;
+      r += c[w];
+    }
+  }
+  __syncthreads();
+  slice_scatter(ids, w0, w1, E, nbits, cnt + wave * E, sorted_pairs, inv_pairs, lane);
+}
+
 int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int32_t n_shared,
                        int32_t row_chunk) {
   const int64_t cap = (int64_t)T * k_max + (int64_t)E * (block_m - 1);
@@ -160,15 +222,27 @@ int32_t max_work_items(int32_t T, int32_t E, int32_t k_max, int32_t block_m, int
   return (int32_t)(routed + shared);
 }
 
+int64_t permute_counts_ints(int32_t T, int32_t E, int32_t k_max) {
+  const int ns = permute_slices(T * k_max);
+  return ns >= kManySlices ? (int64_t)ns * E : 0;
+}
+
 hipError_t launch_permute(const int32_t *ids, int32_t T, int32_t E, int32_t k_max, int32_t block_m,
                           int32_t capacity, int32_t *sorted_pairs, int32_t *expert_offsets,
                           int32_t *block_expert, int32_t *inv_pairs, int32_t *n_blocks,
                           WorkItem *items, int32_t *n_items, int32_t row_chunk, int32_t n_shared,
-                          hipStream_t stream) {
+                          hipStream_t stream, int32_t *counts) {
   const int P = T * k_max;
   const int ns = permute_slices(P);
+  if (ns >= kManySlices && counts) {
+    permute_count_kernel<<<ns, kSliceWaves * kWave, 0, stream>>>(ids, P, E, counts, E);
+    permute_layout_scatter_kernel<<<ns, kSliceWaves * kWave, 0, stream>>>(
+        ids, P, E, block_m, capacity, counts, sorted_pairs, expert_offsets, block_expert,
+        inv_pairs, n_blocks, items, n_items, row_chunk, T, n_shared);
+    return hipGetLastError();
+  }
   if (ns >= kManySlices) {
-    permute_count_kernel<<<ns, kSliceWaves * kWave, 0, stream>>>(ids, P, E, inv_pairs);
+    permute_count_kernel<<<ns, kSliceWaves * kWave, 0, stream>>>(ids, P, E, inv_pairs, kSlice);
     permute_layout_kernel<<<1, 1024, 0, stream>>>(P, E, block_m, capacity, sorted_pairs,
                                                   expert_offsets, block_expert, inv_pairs, n_blocks,
                                                   items, n_items, row_chunk, T, n_shared);

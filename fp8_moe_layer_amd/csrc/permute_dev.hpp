@@ -107,21 +107,12 @@ __device__ __forceinline__ int expert_bits(int E) {
 }
 
 // From the per-expert totals tot[E] (LDS): padded segment offsets off[E+1]
-// (LDS and expert_offsets), the block table, the padding sentinels, n_blocks
-// and the work list.  Every thread of the workgroup (NT of them) calls this;
-// it ends with a workgroup barrier.
+// and work-list offsets item_off[E+1] (LDS).  Every thread of the workgroup
+// calls this; it ends with a workgroup barrier.
 template <int NT>
-__device__ __forceinline__ void build_layout(const int *tot, int *off, int *item_off, int P, int E,
-                                             int bm, int capacity,
-                                             int32_t *__restrict__ sorted_pairs,
-                                             int32_t *__restrict__ expert_offsets,
-                                             int32_t *__restrict__ block_expert,
-                                             int32_t *__restrict__ n_blocks,
-                                             WorkItem *__restrict__ items,
-                                             int32_t *__restrict__ n_items, int row_chunk, int T,
-                                             int S) {
+__device__ __forceinline__ void layout_offsets(const int *tot, int *off, int *item_off, int E,
+                                               int bm, int row_chunk) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sentinel = P;
   // exclusive scan of padded totals and of work-list offsets: lane l holds
   // experts [l*per, (l+1)*per), summed locally, then one wave scan
   if (wave == 0) {
@@ -156,32 +147,59 @@ __device__ __forceinline__ void build_layout(const int *tot, int *off, int *item
     }
   }
   __syncthreads();
+}
 
+// The layout arrays from off / item_off / tot (LDS): part `part` of `parts`
+// of the block table and of the padding sentinels; part 0 also writes
+// expert_offsets, n_blocks and the work list.  No barrier.
+template <int NT>
+__device__ __forceinline__ void layout_write(const int *tot, const int *off, const int *item_off,
+                                             int P, int E, int bm, int capacity,
+                                             int32_t *__restrict__ sorted_pairs,
+                                             int32_t *__restrict__ expert_offsets,
+                                             int32_t *__restrict__ block_expert,
+                                             int32_t *__restrict__ n_blocks,
+                                             WorkItem *__restrict__ items,
+                                             int32_t *__restrict__ n_items, int row_chunk, int T,
+                                             int S, int part, int parts) {
+  const int tid = threadIdx.x;
+  const int sentinel = P;
   const int total = off[E];
   const int nb = total / bm;
   const int nb_cap = (capacity + bm - 1) / bm;
-  for (int e = tid; e <= E; e += NT) expert_offsets[e] = off[e];
-  if (tid == 0) *n_blocks = nb;
+  auto range = [&](int n, int &lo, int &hi) {  // part's share of [0, n)
+    lo = (int)((int64_t)n * part / parts);
+    hi = (int)((int64_t)n * (part + 1) / parts);
+  };
+  int lo, hi;
+  if (part == 0) {
+    for (int e = tid; e <= E; e += NT) expert_offsets[e] = off[e];
+    if (tid == 0) *n_blocks = nb;
+  }
   // a thread per block: its expert is the last segment starting at or before
   // it (off is non-decreasing; empty segments start where the next one does)
-  for (int b = tid; b < nb; b += NT) {
+  range(nb, lo, hi);
+  for (int b = lo + tid; b < hi; b += NT) {
     const int row = b * bm;
-    int lo = 0, hi = E - 1;  // off[lo] <= row < off[E]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= row) lo = mid;
-      else hi = mid - 1;
+    int l = 0, h = E - 1;  // off[l] <= row < off[E]
+    while (l < h) {
+      const int mid = (l + h + 1) >> 1;
+      if (off[mid] <= row) l = mid;
+      else h = mid - 1;
     }
-    block_expert[b] = lo;
+    block_expert[b] = l;
   }
-  for (int e = tid; e < E; e += NT)
+  range(E, lo, hi);
+  for (int e = lo + tid; e < hi; e += NT)
     for (int r = off[e] + tot[e]; r < off[e + 1]; ++r) sorted_pairs[r] = sentinel;
-  for (int b = nb + tid; b < nb_cap; b += NT) block_expert[b] = -1;
-  for (int r = total + tid; r < capacity; r += NT) sorted_pairs[r] = sentinel;
+  range(nb_cap - nb, lo, hi);
+  for (int b = nb + lo + tid; b < nb + hi; b += NT) block_expert[b] = -1;
+  range(capacity - total, lo, hi);
+  for (int r = total + lo + tid; r < total + hi; r += NT) sorted_pairs[r] = sentinel;
 
   // work list for the expert stages: routed segments cut into row_chunk rows,
   // then the shared experts' token rows
-  if (items) {
+  if (items && part == 0) {
     for (int e = tid; e < E; e += NT) {
       const int pad = off[e + 1] - off[e];
       int k = item_off[e];
@@ -196,6 +214,24 @@ __device__ __forceinline__ void build_layout(const int *tot, int *off, int *item
     }
     if (tid == 0) *n_items = item_off[E] + S * per_shared;
   }
+}
+
+// The whole layout in one workgroup: offsets, then every array.  Every
+// thread of the workgroup (NT of them) calls this; it ends with a workgroup
+// barrier.
+template <int NT>
+__device__ __forceinline__ void build_layout(const int *tot, int *off, int *item_off, int P, int E,
+                                             int bm, int capacity,
+                                             int32_t *__restrict__ sorted_pairs,
+                                             int32_t *__restrict__ expert_offsets,
+                                             int32_t *__restrict__ block_expert,
+                                             int32_t *__restrict__ n_blocks,
+                                             WorkItem *__restrict__ items,
+                                             int32_t *__restrict__ n_items, int row_chunk, int T,
+                                             int S) {
+  layout_offsets<NT>(tot, off, item_off, E, bm, row_chunk);
+  layout_write<NT>(tot, off, item_off, P, E, bm, capacity, sorted_pairs, expert_offsets,
+                   block_expert, n_blocks, items, n_items, row_chunk, T, S, 0, 1);
   __syncthreads();
 }
 

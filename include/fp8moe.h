@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FP8MOE_ABI_VERSION 5
+#define FP8MOE_ABI_VERSION 6
 
 typedef int32_t moe_status;
 enum {
@@ -206,6 +206,22 @@ moe_status moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_
                        int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
                        int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
                        int32_t *n_blocks, void *stream);
+
+/* The same permutation with a device workspace for the per-slice expert
+ * counts of large batches (T*k_max >= 4096 pairs, cut into slices of 1024):
+ * with it the permutation takes two launches instead of three; the outputs
+ * are those of moe_permute bit for bit.  moe_permute_workspace_bytes gives
+ * the size (0 when the batch needs none: then workspace may be NULL); the
+ * workspace must be 16-byte aligned, caller-owned, and not touched by
+ * anything else while the work is in flight.  MOE_ERR_WORKSPACE when it is
+ * missing or too small; other errors as moe_permute.  moe_fused_forward runs
+ * this form on its own workspace. */
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t k_max);
+moe_status moe_permute_ws(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k_max,
+                          int32_t block_m, int32_t capacity, int32_t *sorted_pairs,
+                          int32_t *expert_offsets, int32_t *block_expert, int32_t *inv_pairs,
+                          int32_t *n_blocks, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /* "Expert rows" layout used by the three expert stages below: rows
  * [0, capacity) follow sorted_pairs (padding rows hold garbage or zeros);

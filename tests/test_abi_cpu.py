@@ -48,7 +48,7 @@ def test_debug_library_rejects_on_the_host_like_the_release_one():
 
 
 def test_abi_version_and_status_strings():
-    assert fp8.ABI_VERSION == 5
+    assert fp8.ABI_VERSION == 6
     assert fp8._status_str(ERR_DEVICE_CHECK) == b"device check failed (debug build)"
     assert fp8._status_str(0) == b"ok"
     assert fp8._status_str(ERR_WORKSPACE) == b"workspace too small"
@@ -203,6 +203,19 @@ def test_step_entry_points_reject_bad_arguments():
     assert fp8._permute(FAKE, 4, 8, 2, 16, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE
     assert fp8._permute(FAKE, 4, 8, 2, 3, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE
     assert fp8._permute(FAKE, 4, 8, 2, 16, 1000, None, FAKE, FAKE, FAKE, FAKE, None) == ERR_NULL
+    # the workspace form: 4096 pairs or more need slice counts (4 slices x E ints)
+    assert fp8.permute_workspace_bytes(16, 8, 2) == 0
+    assert fp8.permute_workspace_bytes(2048, 64, 2) == 4 * 64 * 4
+    assert fp8.permute_workspace_bytes(8192, 64, 6) == 48 * 64 * 4
+    cap = fp8.capacity(2048, 64, 2, 16)
+    assert fp8._permute_ws(FAKE, 2048, 64, 2, 16, cap, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                           None) == ERR_WORKSPACE
+    assert fp8._permute_ws(FAKE, 2048, 64, 2, 16, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100,
+                           None) == ERR_WORKSPACE
+    assert fp8._permute_ws(FAKE, 2048, 64, 2, 16, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 1024,
+                           None) == ERR_ALIGN
+    assert fp8._permute_ws(FAKE, 2048, 64, 2, 16, cap - 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024,
+                           None) == ERR_SHAPE
     dm = _dims()
     w = fp8._Weights(*([FAKE] * 12))
     cap = fp8.capacity(16, 8, 2, 16)

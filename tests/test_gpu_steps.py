@@ -179,13 +179,18 @@ def test_topk_bit_exact(T, E, k, var):
                                           (8192, 64, 6, 128, False), (3, 512, 4, 16, True),
                                           (2053, 64, 8, 16, False), (4096, 128, 8, 16, False),
                                           (5000, 512, 8, 1, True)])
-def test_permute_bit_exact(T, E, k, bm, var):
+@pytest.mark.parametrize("workspace", [False, True])
+def test_permute_bit_exact(T, E, k, bm, var, workspace):
+    """moe_permute, and moe_permute_ws (the two-launch form for batches of four
+    or more 1024-pair slices: layout and scatter in one launch over the slice
+    counts in the workspace), against the oracle, every array bit for bit."""
     rng = np.random.default_rng(T * 3 + E)
     l = rng.standard_normal((T, E)).astype(np.float32)
     l[:, 0] += 2.0  # a hot expert
     kpt = rng.integers(1, k + 1, T).astype(np.int32) if var else None
     ids, _ = oracle.route_topk(l, k, kpt)
-    p = lib().permute(torch.from_numpy(ids).to(dev()), E, bm)
+    p = lib().permute(torch.from_numpy(ids).to(dev()), E, bm, workspace=workspace)
+    torch.cuda.synchronize()
     po = oracle.permute(ids, E, bm)
     for key in ("sorted_pairs", "expert_offsets", "block_expert", "inv_pairs", "n_blocks"):
         np.testing.assert_array_equal(to_np(p[key]), po[key], err_msg=key)
