@@ -73,6 +73,9 @@ def parse(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     p.add_argument("--points", default="all", choices=["all", "none"],
                    help="also time the other layer shapes (all) or only the selected one (none)")
+    p.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                   help="untimed forwards for this long before each timed loop (GPU clocks "
+                        "ramp up after idle); 0: none")
     p.add_argument("--point-steps", type=int, default=50)
     p.add_argument("--point-warmup", type=int, default=20)
     p.add_argument("--parity-tokens", type=int, default=64,
@@ -304,10 +307,35 @@ class Shape:
         self.dw = None
 
 
+# Untimed work before every timed loop, in ms of wall time (--settle-ms).
+# The GPU lowers its clocks within ~50 ms of idling (host-side set-up, the
+# oracle's parity checks between points) and takes ~10-20 ms of load to come
+# back: measured on the Mixtral-shaped T=256 layer, a loop of 5 + 20 steps
+# started after 50 ms, 0.2 s or 1 s of idle ran 290-294 us per step, the next
+# such loop 273-274 us and later ones 266-268 us, while a loop started after
+# 100 ms of back-to-back forwards ran 266 us.  The timed steps then measure
+# the layer at the clocks it runs at under load, whatever the warm-up count.
+SETTLE_MS = 100.0
+
+
+def settle(torch, fn):
+    """Calls fn (one untimed forward) in batches of eight, synchronising after
+    each batch, until SETTLE_MS of wall time have passed; returns the calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(torch, layers, x, kpt, out, ids, steps, warmup, sh):
     """Mean ms per step over `steps` back-to-back forwards (HIP events on the
-    library's stream), after `warmup` untimed ones."""
+    library's stream), after the settle phase and `warmup` untimed ones."""
     R = len(layers)
+    settle(torch, lambda i: layers[i % R].forward(x, k_per_token=kpt, out=out, topk_ids=ids))
     for i in range(warmup):
         layers[i % R].forward(x, k_per_token=kpt, out=out, topk_ids=ids)
     torch.cuda.synchronize()
@@ -444,6 +472,7 @@ def _capture(torch, lay, x, kpt, out, ids):
 
 
 def _time_replays(torch, gs, steps, warmup):
+    settle(torch, lambda i: gs[i % len(gs)].replay())
     for i in range(warmup):
         gs[i % len(gs)].replay()
     torch.cuda.synchronize()
@@ -508,7 +537,9 @@ def shape_spec(wl, cfg, Tmax):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = max(0.0, args.settle_ms)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py runs on one GPU only: this build measures the layer on a single MI355X "
@@ -628,6 +659,7 @@ def main():
                 Ds = [int(len(np.unique(gi[idx[b:b + gb]][gi[idx[b:b + gb]] >= 0])))
                       for b in range(0, pool, gb)]
                 bout = torch.empty((gb, spec.d), dtype=torch.float32, device=dev)
+                settle(torch, lambda i: glay.forward(bx[i % len(bx)], out=bout))
                 for i in range(args.warmup):
                     glay.forward(bx[i % len(bx)], out=bout)
                 ev = HipEvents(2)
@@ -659,6 +691,8 @@ def main():
             return tlays[k]
 
         def time_runs(runs):
+            settle(torch, lambda i: runs[i % len(runs)][0].forward(
+                runs[i % len(runs)][1], k_per_token=runs[i % len(runs)][2], out=runs[i % len(runs)][3]))
             for i in range(max(1, args.warmup // len(runs))):
                 for lay_, xb, kb, ob in runs:
                     lay_.forward(xb, k_per_token=kb, out=ob)
@@ -807,6 +841,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
