@@ -68,14 +68,18 @@ struct GemmArgs {
   float *hsc = nullptr;
 };
 
+// real: the item's rows that hold pairs (the rest of its rows are segment
+// padding, whose h and y no stage reads: the epilogues skip their stores);
+// without a work list every row counts as real.
 __device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, int &expert,
-                                             int &row0, int &rows) {
+                                             int &row0, int &rows, int &real) {
   if (rs.items) {
     if (item_id >= *rs.n_items) return false;
     const WorkItem it = rs.items[item_id];
     expert = it.expert;
     row0 = it.row0;
     rows = it.rows;
+    real = min(max(it.real, 0), rows);
     // an item lies inside its expert's rows (routed: [0, capacity); shared
     // expert s: [capacity + s*T, +T))
     if constexpr (kDebugChecks) {
@@ -94,6 +98,7 @@ __device__ __forceinline__ bool resolve_item(const RowSpace &rs, int item_id, in
       row0 = rs.capacity + (expert - rs.E) * rs.T;
       rows = rs.T;
     }
+    real = rows;
   }
   return rows > 0;
 }
@@ -242,13 +247,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
   const RowSpace &rs = g.rs;
   const int N = GATEUP ? rs.f : rs.d;
   const int kg = lane >> 4;
-  // Lane (ln, kg) holds rows m*16 + kg*4 + i of channel wo.ch[nb].  Only the
-  // last row group of a pass can run past the item's rows (a pass of
-  // 16*MSUB real rows takes the unmasked path); a padding row has scale 0
-  // (and zero activations): 0 out.  The store address advances by one row
-  // per element (no table of row offsets).  Stores are non-temporal: the
-  // output stream does not push the weight stream's neighbours (activation
-  // rows, tables) out of L2.
+  // Lane (ln, kg) holds rows m*16 + kg*4 + i of channel wo.ch[nb].  prow and
+  // msub here count the pass's rows to store: the rows that hold pairs (an
+  // expert segment's padding rows follow its last pair, and no stage reads
+  // their h or y), so only the last stored row group is masked (a pass of
+  // 16*MSUB stored rows takes the unmasked path).  The store address
+  // advances by one row per element (no table of row offsets).  Stores are
+  // non-temporal: the output stream does not push the weight stream's
+  // neighbours (activation rows, tables) out of L2.
   const bool full = prow == 16 * MSUB;
   const bool to16 = O16 == 1 || (O16 < 0 && g.out16 != nullptr);
   if (GATEUP) {
@@ -370,9 +376,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, const v4f (&acc
 // workgroup barrier (the loader wave takes it too) a row's amax is the
 // maximum over the waves, and hq = e4m3(h * (448/amax)), hsc = amax/448 --
 // the separate requantisation's operations on the same h, so the same codes
-// and scales bit for bit, with no fp32 h in memory.  Every row of the pass
-// is written: a padding row has h = 0, so codes 0 and scale 1 (the down
-// projection never reads them).
+// and scales bit for bit, with no fp32 h in memory.  prow and msub count the
+// rows to store (those that hold pairs): the down projection gives segment
+// padding rows zero activations and scale 0 without reading hq or hsc.
 template <int MSUB, int NB, bool NT>
 __device__ __forceinline__ void gemm_epilogue_rq(const GemmArgs &g, const v4f (&acc)[MSUB][NB],
                                                  const WOperands<NB, true, NT> &wo,
@@ -519,8 +525,8 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
   bid /= g.splits;
   const int tile = bid % n_tiles;
   const int item_id = bid / n_tiles;
-  int expert, row0, rows;
-  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  int expert, row0, rows, real;
+  if (!resolve_item(rs, item_id, expert, row0, rows, real)) return;
   const int k_begin = split * g.ksplit;
   const int k_end = min(K, k_begin + g.ksplit);
   if (k_begin >= k_end) return;
@@ -676,12 +682,14 @@ __device__ __forceinline__ void wsgemm_tile(const GemmArgs &g, int bid, uint8_t 
       }
     }
 
+    // stores stop at the pass's last row that holds a pair
+    const int srow = min(max(real - p0, 0), prow);
     if constexpr (RQ) {
       static_assert(GATEUP, "the fused requantisation follows the gate/up GEMM");
       gemm_epilogue_rq<MSUB, NB, NT>(g, acc, wo, rsc, reinterpret_cast<float *>(abuf + C::LDS), row0,
-                                     p0, prow, msub, lane, wave, W);
+                                     p0, srow, (srow + 15) >> 4, lane, wave, W);
     } else {
-      gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
+      gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, wo, rsc, row0, p0, srow, (srow + 15) >> 4, split, lane);
     }
   }
 }
@@ -771,8 +779,8 @@ __device__ __forceinline__ void ares_tile(const GemmArgs &g, int bid, uint8_t *l
   const int item_id = bid / n_groups;
   const int t_begin = (bid - item_id * n_groups) * g.ntg;
   const int t_end = min(n_tiles, t_begin + g.ntg);
-  int expert, row0, rows;
-  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  int expert, row0, rows, real;
+  if (!resolve_item(rs, item_id, expert, row0, rows, real)) return;
   if (t_begin >= t_end) return;
   const int nks = (K + 127) >> 7;
   const int ksp = (nks + PF - 1) / PF * PF;  // K steps padded to the ring depth (zero A)
@@ -882,7 +890,7 @@ __device__ __forceinline__ void ares_tile(const GemmArgs &g, int bid, uint8_t *l
       const int i = min(cur.ch[nb], N - 1) - c_first;
       ep.wsc[nb] = GATEUP ? wsl[2 * i + (nb & 1)] : wsl[i];
     }
-    gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, ep, rsc, row0, 0, rows, msub, 0, lane);
+    gemm_epilogue<MSUB, NB, GATEUP, NT>(g, acc, ep, rsc, row0, 0, real, (real + 15) >> 4, 0, lane);
     if (has_next) cur = nxt;
   }
 }
@@ -926,8 +934,8 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *abu
   bid /= g.splits;
   const int tile = bid % n_tiles;
   const int item_id = bid / n_tiles;
-  int expert, row0, rows;
-  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  int expert, row0, rows, real;
+  if (!resolve_item(rs, item_id, expert, row0, rows, real)) return;
   const int k_begin = split * g.ksplit;
   const int k_end = min(K, k_begin + g.ksplit);
   if (k_begin >= k_end) return;
@@ -1045,7 +1053,9 @@ __device__ __forceinline__ void pf_tile(const GemmArgs &g, int bid, uint8_t *abu
         barrier_lds();
       }
     }
-    gemm_epilogue<MSUB, NB, GATEUP, false, O16>(g, acc, wo, rsc, row0, p0, prow, msub, split, lane);
+    const int srow = min(max(real - p0, 0), prow);  // stores stop at the last row with a pair
+    gemm_epilogue<MSUB, NB, GATEUP, false, O16>(g, acc, wo, rsc, row0, p0, srow, (srow + 15) >> 4, split,
+                                                lane);
   }
 }
 
@@ -1066,8 +1076,8 @@ __device__ __forceinline__ void down_f32_tile(const GemmArgs &g, int bid, int ti
   const int n_tiles = (d + 63) >> 6;
   const int item_id = bid / n_tiles;
   const int tile = bid - item_id * n_tiles;
-  int expert, row0, rows;
-  if (!resolve_item(rs, item_id, expert, row0, rows)) return;
+  int expert, row0, rows, real;
+  if (!resolve_item(rs, item_id, expert, row0, rows, real)) return;
   const bool shared = expert >= rs.E;
   const size_t ex = (size_t)(shared ? expert - rs.E : expert);
   const uint8_t *wd = (shared ? g.w.ws_down : g.w.w_down) + ex * d * (size_t)KT * 128;

@@ -21,7 +21,7 @@ struct WorkItem {
   int32_t expert;
   int32_t row0;
   int32_t rows;
-  int32_t pad;
+  int32_t real;  // the first `real` rows hold (token, slot) pairs, the rest padding
 };
 
 struct ExpertWeights {

@@ -105,8 +105,8 @@ __global__ __launch_bounds__(kGemmMaxThreads) void wsgemm2_kernel(GemmArgs g) {
   const int ch_wg = W * (GATEUP ? 16 : 32);
   const int n_tiles = (N + ch_wg - 1) / ch_wg;
   const int item_id = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / g.splits) / n_tiles);
-  int expert, row0, rows;
-  if (!resolve_item(g.rs, item_id, expert, row0, rows)) return;
+  int expert, row0, rows, real;
+  if (!resolve_item(g.rs, item_id, expert, row0, rows, real)) return;
   if (__builtin_amdgcn_readfirstlane(rows) <= 16 * MS)
     wsgemm_tile<MS, 2, GATEUP, NT>(g, blockIdx.x, abuf);
   else

@@ -204,13 +204,15 @@ __device__ __forceinline__ void layout_write(const int *tot, const int *off, con
       const int pad = off[e + 1] - off[e];
       int k = item_off[e];
       for (int r0 = 0; r0 < pad; r0 += row_chunk, ++k)
-        items[k] = WorkItem{e, off[e] + r0, min(row_chunk, pad - r0), 0};
+        items[k] = WorkItem{e, off[e] + r0, min(row_chunk, pad - r0),
+                            max(0, min(row_chunk, tot[e] - r0))};
     }
     const int per_shared = (T + row_chunk - 1) / row_chunk;
     for (int i = tid; i < S * per_shared; i += NT) {
       const int s = i / per_shared, c = i % per_shared;
       const int r0 = c * row_chunk;
-      items[item_off[E] + i] = WorkItem{E + s, capacity + s * T + r0, min(row_chunk, T - r0), 0};
+      const int rows = min(row_chunk, T - r0);
+      items[item_off[E] + i] = WorkItem{E + s, capacity + s * T + r0, rows, rows};
     }
     if (tid == 0) *n_items = item_off[E] + S * per_shared;
   }
