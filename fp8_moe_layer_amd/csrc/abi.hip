@@ -307,7 +307,7 @@ struct Layout {
   bool nt_gu, nt_dn;  // non-temporal weight loads
   GemmPlan gu, dn;
   bool ares_gu, ares_dn;     // A-resident tiles (short K)
-  bool rq_gu;                // gate/up with the requantisation fused in (f <= 224)
+  bool rq_gu;                // gate/up with the requantisation fused in (f <= 16*kRqMaxWaves)
   int32_t ntg_gu, ntg_dn;    // their N-tiles per workgroup
 };
 

@@ -1,7 +1,6 @@
 """The gate/up GEMM with the per-row e4m3 requantisation fused into its
-epilogue (north_star: "a fused SiLU*up epilogue with per-token fp8
-requantisation"), used where one workgroup's channels span a row's whole f
-(f <= 224, e.g. the MoE-Prism sub-experts with f = 192).
+SiLU*up epilogue, used where one workgroup's channels span a row's whole f
+(f <= 192, e.g. the MoE-Prism sub-experts with f = 192).
 
 The fused epilogue forms h with the same operations as the h epilogue and
 requantises it with the separate requantisation's operations, so the layer's
